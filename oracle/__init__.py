@@ -1,0 +1,131 @@
+"""ORACLE -- test infrastructure only.
+
+Plain CPU causal grouped-query attention (oracle/oracle.c, built with gcc in
+fp64 and fp32) used to check the HIP path.  Only tests/, the smoke check and
+the bench's CPU-baseline leg may import it; the library never does, and the
+two share no code.
+
+Inputs are bf16 bit patterns (numpy uint16): q [B, Hq, q_len, D] and
+k/v [B, Hkv, kv_capacity, D].  Query row r sits at position
+kv_len - q_len + r and attends to keys 0..pos of KV head h // (Hq // Hkv).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIBS = {
+    "f64": os.path.join(_HERE, "liboracle_f64.so"),
+    "f32": os.path.join(_HERE, "liboracle_f32.so"),
+}
+_REAL = {"f64": "double", "f32": "float"}
+_loaded: dict = {}
+
+
+def build() -> None:
+    """Compile both precisions of the oracle (always recompiles)."""
+    for prec, path in _LIBS.items():
+        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-pthread", f"-DKBO_REAL={_REAL[prec]}", f"-DKBO_SUFFIX=_{prec}", _SRC,
+               "-o", path + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(path + ".tmp", path)
+
+
+def bind(path: str, prec: str):
+    """(attention, weights) C entry points of an oracle build at `path`."""
+    lib = ctypes.CDLL(path)
+    f = getattr(lib, f"kbo_attention_{prec}")
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 7 + [ctypes.c_double, ctypes.c_void_p,
+                                                                 ctypes.c_int64, ctypes.c_void_p,
+                                                                 ctypes.c_int]
+    f.restype = ctypes.c_int
+    w = getattr(lib, f"kbo_weights_{prec}")
+    w.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 7 + [ctypes.c_double, ctypes.c_int64,
+                                                                 ctypes.c_void_p]
+    w.restype = ctypes.c_int
+    return f, w
+
+
+def _lib(prec: str):
+    if prec not in _loaded:
+        if not os.path.exists(_LIBS[prec]):
+            build()
+        _loaded[prec] = bind(_LIBS[prec], prec)
+    return _loaded[prec]
+
+
+def _threads(n):
+    if n:
+        return int(n)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _check(q, k, v):
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if x.dtype != np.uint16 or x.ndim != 4 or not x.flags.c_contiguous:
+            raise ValueError(f"{name} must be a contiguous 4-D uint16 (bf16 bits) array")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError("shape mismatch")
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_len: int | None = None,
+              scale: float | None = None, rows=None, precision: str = "f64",
+              threads: int | None = None, entry=None) -> np.ndarray:
+    """Attention output as float64.
+
+    Without rows: shape [B, Hq, q_len, D].  With rows (flat ids
+    b*Hq*q_len + h*q_len + r): shape [len(rows), D].
+    """
+    _check(q, k, v)
+    B, Hq, q_len, D = q.shape
+    Hkv, cap = k.shape[1], k.shape[2]
+    kv_len = cap if kv_len is None else int(kv_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    f, _ = entry if entry is not None else _lib(precision)
+    if rows is None:
+        out = np.empty((B, Hq, q_len, D), dtype=np.float64)
+        rows_ptr, n = None, B * Hq * q_len
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((rows.size, D), dtype=np.float64)
+        rows_ptr, n = rows.ctypes.data, rows.size
+    rc = f(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Hq, Hkv, q_len, kv_len, cap, D, scale,
+           rows_ptr, n, out.ctypes.data, _threads(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out
+
+
+def weights(q, k, v, row: int, kv_len: int | None = None, scale: float | None = None,
+            precision: str = "f64", entry=None) -> np.ndarray:
+    """Normalised softmax weights of one row (flat id), length pos + 1."""
+    _check(q, k, v)
+    B, Hq, q_len, D = q.shape
+    Hkv, cap = k.shape[1], k.shape[2]
+    kv_len = cap if kv_len is None else int(kv_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    r = row % q_len
+    pos = kv_len - q_len + r
+    out = np.empty(pos + 1, dtype=np.float64)
+    _, w = entry if entry is not None else _lib(precision)
+    rc = w(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Hq, Hkv, q_len, kv_len, cap, D, scale, row,
+           out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out
+
+
+def row_flops(positions) -> int:
+    """Algorithmic FLOPs of the rows at the given positions: 4*D*(pos+1) each with D=128."""
+    positions = np.asarray(positions, dtype=np.int64)
+    return int((4 * 128 * (positions + 1)).sum())

@@ -1,0 +1,44 @@
+"""The seeded input generator: deterministic, thread-split independent, N(0,1)."""
+import numpy as np
+
+import kb_gen
+
+
+def test_thread_split_independent():
+    a = kb_gen.normal_bf16(17, kb_gen.TID_Q, (3, 5, 1000), threads=1)
+    b = kb_gen.normal_bf16(17, kb_gen.TID_Q, (3, 5, 1000), threads=7)
+    assert np.array_equal(a, b)
+    for i in (0, 1, 4999, 14999):
+        assert kb_gen.normal_bf16_at(17, kb_gen.TID_Q, i) == a.ravel()[i]
+
+
+def test_streams_differ_and_moments():
+    q = kb_gen.normal_bf16(2, kb_gen.TID_Q, (1 << 20,))
+    k = kb_gen.normal_bf16(2, kb_gen.TID_K, (1 << 20,))
+    q3 = kb_gen.normal_bf16(3, kb_gen.TID_Q, (1 << 20,))
+    assert not np.array_equal(q, k) and not np.array_equal(q, q3)
+    x = kb_gen.bf16_bits_to_f32(q).astype(np.float64)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+    assert np.isfinite(x).all()
+
+
+def test_outliers_exact_scaling():
+    ch = kb_gen.outlier_channels(5, 4, 128)
+    assert len(set(ch.tolist())) == 4 and ch.min() >= 0 and ch.max() < 128
+    q, k, v = kb_gen.attention_inputs(5, 1, 64, 4, 1, 128)
+    q0, k0, v0 = kb_gen.attention_inputs(5, 1, 64, 4, 1, 128, outliers=0)
+    q1, k1, v1 = kb_gen.attention_inputs(5, 1, 64, 4, 1, 128, outliers=4)
+    f = kb_gen.bf16_bits_to_f32
+    assert np.array_equal(f(q1)[..., ch], 8 * f(q0)[..., ch])
+    assert np.array_equal(f(k1)[..., ch], 8 * f(k0)[..., ch])
+    rest = np.setdiff1d(np.arange(128), ch)
+    assert np.array_equal(q1[..., rest], q0[..., rest]) and np.array_equal(v1, v0)
+
+
+def test_bf16_round_trip():
+    x = np.array([1.0, -2.5, 1 + 2 ** -8, 1 + 3 * 2 ** -9, 3.0e38], dtype=np.float32)
+    b = kb_gen.f32_to_bf16_bits(x)
+    y = kb_gen.bf16_bits_to_f32(b)
+    assert y[0] == 1.0 and y[1] == -2.5
+    assert y[2] == 1.0            # tie rounds to even
+    assert y[3] == 1 + 2 ** -7    # above the tie rounds up

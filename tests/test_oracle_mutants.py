@@ -1,0 +1,89 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies oracle/oracle.c, applies one plausible mistake (a dropped
+term, a wrong sign or index, a transposed operand, an off-by-one mask, a wrong
+stride), builds it with gcc in a temporary folder and runs a compact battery
+of the same pins used in test_oracle_pins.py.  The unmodified copy must pass
+the battery and every mutant must fail it.
+"""
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import kb_gen
+import oracle
+from test_oracle_pins import brute_force, f32, inputs
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "gqa_modulo_mapping": [("h / (p->n_q_heads / p->n_kv_heads)", "h % p->n_kv_heads")],
+    "top_left_causal": [("const int64_t pos = p->kv_len - p->q_len + r;", "const int64_t pos = r;")],
+    "dropped_scale": [("s[j] = p->scale * dot;", "s[j] = dot;")],
+    "reversed_k_channels": [("widen(kbase[j * D + d])", "widen(kbase[j * D + (D - 1 - d)])")],
+    "v_read_from_k": [("widen(vbase[j * D + d])", "widen(kbase[j * D + d])")],
+    "dropped_normalisation": [("for (int64_t d = 0; d < D; ++d) out[d] /= l;", "")],
+    "exp_sign": [("s[j] = kbo_exp(s[j] - m);", "s[j] = kbo_exp(m - s[j]);")],
+    "sees_one_future_key": [("j <= pos;", "j <= pos + (pos + 1 < p->kv_len);")],
+    "drops_diagonal_key": [("j <= pos;", "j < pos + (pos == 0);")],
+    "dropped_first_channel": [("for (int64_t d = 0; d < D; ++d) dot +=", "for (int64_t d = 1; d < D; ++d) dot +=")],
+    "kv_stride_uses_length": [("(b * p->n_kv_heads + g) * p->kv_capacity * D",
+                               "(b * p->n_kv_heads + g) * p->kv_len * D")],
+    "weights_not_normalised": [("w[j] = (double)(s[j] / l);", "w[j] = (double)s[j];")],
+}
+
+
+def build_variant(tmp_path, name, edits):
+    text = open(SRC).read()
+    for old, new in edits:
+        assert old in text, f"mutation anchor not found: {old!r}"
+        text = text.replace(old, new)
+    src = tmp_path / f"{name}.c"
+    lib = tmp_path / f"lib{name}.so"
+    src.write_text(text)
+    subprocess.run(["gcc", "-std=c11", "-O1", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
+                    "-DKBO_REAL=double", "-DKBO_SUFFIX=_f64", str(src), "-o", str(lib), "-lm"], check=True)
+    return oracle.bind(str(lib), "f64")
+
+
+def battery(entry) -> bool:
+    """True when the build passes every pin in the compact battery."""
+    ok = True
+    # brute force, including GQA, a partitioned split and a cache larger than kv_len
+    for (B, Hq, Hkv, q_len, kv_len, D, cap) in [(2, 4, 2, 5, 5, 8, 5), (2, 4, 2, 3, 9, 8, 12),
+                                                (1, 8, 2, 6, 6, 16, 6)]:
+        q, k, v = inputs(1000 + q_len, B, Hq, Hkv, q_len, kv_len, D, cap=cap)
+        ref = brute_force(q, k, v, kv_len, 1 / math.sqrt(D))
+        got = oracle.attention(q, k, v, kv_len=kv_len, entry=entry)
+        ok &= bool(np.allclose(got, ref, rtol=1e-12, atol=1e-12))
+    # rows sum to one
+    q, k, v = inputs(5, 1, 4, 2, 20, 20, 8)
+    for row in (0, 7, 19, 45):
+        w = oracle.weights(q, k, v, row, entry=entry)
+        ok &= abs(1 - math.fsum(w)) < 1e-12
+    # causality
+    base = oracle.attention(q, k, v, entry=entry)
+    k2 = k.copy()
+    k2[:, :, 11:] = kb_gen.normal_bf16(77, 2, k2[:, :, 11:].shape)
+    ok &= bool(np.array_equal(oracle.attention(q, k2, v, entry=entry)[:, :, :11], base[:, :, :11]))
+    # GQA == MHA with repeated heads
+    mha = oracle.attention(q, np.ascontiguousarray(np.repeat(k, 2, axis=1)),
+                           np.ascontiguousarray(np.repeat(v, 2, axis=1)), entry=entry)
+    ok &= bool(np.array_equal(base, mha))
+    # constant V and row 0
+    vc = kb_gen.f32_to_bf16_bits(np.full(v.shape, 1.5, dtype=np.float32))
+    ok &= bool(np.allclose(oracle.attention(q, k, vc, entry=entry), 1.5, rtol=1e-13, atol=0))
+    ok &= bool(np.array_equal(base[:, :, 0], np.repeat(f32(v[:, :, 0]), 2, axis=1)))
+    return ok
+
+
+def test_unmodified_copy_passes(tmp_path):
+    assert battery(build_variant(tmp_path, "clean", []))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    assert not battery(build_variant(tmp_path, name, MUTANTS[name])), f"pins missed mutant {name}"
