@@ -1,0 +1,120 @@
+/*
+ * kb_attn -- bitwise-aligned causal grouped-query attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operator is the unified attention of the KernelBraid / AReaL-TIK README:
+ *   - "Features": BF16, causal, contiguous [batch, heads, sequence, head_dim]
+ *     tensors, 32 query heads, 8 KV heads, head_dim 128;
+ *   - "Usage": a causal full-sequence forward (unified_prefill) and a
+ *     one-token decode over the same KV context (unified_decode) whose output
+ *     equals the last prefill row bit for bit; the output has the shape of q;
+ *   - "Method" / "Advantages": one numerical contract links full-sequence
+ *     prefill, partitioned forward and one-token decode, so all three give
+ *     bitwise-identical outputs for the same inputs and context.
+ *
+ * Numerical contract (shared by every entry point): for the query row at
+ * absolute position pos (keys 0..pos visible, KV head = q head / 4),
+ * keys are visited in tiles of KB_ATTN_KV_TILE keys from key 0 and grouped in
+ * chunks of KB_ATTN_KV_CHUNK keys; each chunk runs an fp32 online softmax over
+ * its tiles in order, and chunk results are folded in chunk order.  The output
+ * bits depend only on (q row, K/V rows 0..pos, scale).
+ *
+ * Conventions for every entry point:
+ *   - q, k, v, o, k_cache, v_cache are DEVICE pointers of the current HIP
+ *     device to bf16 values (raw 16-bit patterns), 16-byte aligned.
+ *   - q and o are [batch, n_q_heads, q_len, head_dim] contiguous.
+ *   - k/v (prefill) are [batch, n_kv_heads, seq_len, head_dim] contiguous;
+ *     k_cache/v_cache are [batch, n_kv_heads, kv_capacity, head_dim]
+ *     contiguous, of which rows 0..kv_len-1 are read (the caller writes the
+ *     current token(s) before the call; the library never writes the cache).
+ *   - head_dim must be 128 and n_q_heads must equal 4 * n_kv_heads.
+ *   - scale multiplies <q, k>; it must be finite and > 0 (1/sqrt(128) in the
+ *     README's workloads, whose API takes no scale).
+ *   - The caller owns every buffer; the library allocates nothing, keeps no
+ *     state and is thread-safe.  Calls are asynchronous on `stream` (0 = the
+ *     null stream) and return once the work is enqueued.
+ *   - o must not overlap any input.
+ *   - Every argument is checked before anything is launched; on error nothing
+ *     is launched and a negative KB_ATTN_ERR_* code is returned.
+ */
+#ifndef KB_ATTN_H
+#define KB_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KB_ATTN_KV_TILE 64
+#define KB_ATTN_KV_CHUNK 1024
+#define KB_ATTN_CONTRACT_VERSION 1
+
+enum {
+    KB_ATTN_OK = 0,
+    KB_ATTN_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad scale */
+    KB_ATTN_ERR_UNSUPPORTED = -2, /* head_dim != 128 or n_q_heads != 4 * n_kv_heads */
+    KB_ATTN_ERR_LENGTH = -3,      /* q_len < 1, q_len > kv_len or kv_len > kv_capacity */
+    KB_ATTN_ERR_ALIGNMENT = -4,   /* a pointer is not 16-byte aligned */
+    KB_ATTN_ERR_DEVICE = -5,      /* a pointer is not device memory of the current device */
+    KB_ATTN_ERR_WORKSPACE = -6,   /* decode workspace missing or too small */
+    KB_ATTN_ERR_ALIAS = -7,       /* the output overlaps an input or the workspace */
+    KB_ATTN_ERR_HIP = -8          /* a HIP call or kernel launch failed */
+};
+
+/*
+ * Causal full-sequence forward ("Usage": unified_prefill).  Query row r sits
+ * at position r and attends to keys 0..r of KV head h / 4.
+ * q, o: [batch, n_q_heads, seq_len, 128]; k, v: [batch, n_kv_heads, seq_len, 128].
+ */
+int kb_attn_prefill(const void* q, const void* k, const void* v, void* o, int64_t batch,
+                    int64_t seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    float scale, hipStream_t stream);
+
+/*
+ * Partitioned (chunked) forward ("Method": partitioned forward execution;
+ * "Usage": prompt/answer splits).  A chunk of q_len query rows against a
+ * cache holding kv_len keys; row r sits at position kv_len - q_len + r
+ * (bottom-right causal), so a sequence cut into chunks reproduces the prefill
+ * rows bit for bit.
+ * q, o: [batch, n_q_heads, q_len, 128]; caches: [batch, n_kv_heads, kv_capacity, 128].
+ */
+int kb_attn_partitioned(const void* q, const void* k_cache, const void* v_cache, void* o,
+                        int64_t batch, int64_t q_len, int64_t kv_len, int64_t kv_capacity,
+                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                        hipStream_t stream);
+
+/*
+ * One-token decode ("Usage": unified_decode over the full KV context).  The
+ * single query row sits at position kv_len - 1.  When kv_len exceeds one
+ * chunk the keys are split by chunk across workgroups; the partial results go
+ * to `workspace` (fp32, caller owned, at least
+ * kb_attn_decode_workspace_bytes(...) bytes, device memory) and are folded in
+ * chunk order, the same order the prefill kernel uses.  workspace may be
+ * NULL when that size is 0.  Concurrent calls need separate workspaces.
+ * q, o: [batch, n_q_heads, 1, 128]; caches: [batch, n_kv_heads, kv_capacity, 128].
+ */
+int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch,
+                   int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
+                   int32_t head_dim, float scale, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* Workspace bytes kb_attn_decode needs (0 when kv_len fits in one chunk;
+ * 0 for invalid sizes). */
+size_t kb_attn_decode_workspace_bytes(int64_t batch, int64_t kv_len, int32_t n_q_heads,
+                                      int32_t head_dim);
+
+/* Static description of an error code (never NULL). */
+const char* kb_attn_strerror(int code);
+
+/* The contract constants compiled into the library (any pointer may be NULL). */
+void kb_attn_contract(int32_t* kv_tile, int32_t* kv_chunk, int32_t* version);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KB_ATTN_H */

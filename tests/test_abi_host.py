@@ -1,0 +1,126 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol and
+rejects malformed calls before touching the GPU (CPU only, no compute)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bitwise_aligned_causal_amd as kb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kb_attn.h")
+
+OK, INVALID, UNSUPPORTED, LENGTH, ALIGN, DEVICE, WORKSPACE, ALIAS, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+SCALE = 128 ** -0.5
+
+# fake, aligned, non-overlapping "device" addresses: every call below must
+# return before dereferencing or querying them
+Q, K, V, O, W = (ctypes.c_void_p(0x10_0000_0000 + i * 0x1_0000_0000) for i in range(5))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*|void)\s+(kb_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"kb_attn_prefill", "kb_attn_partitioned", "kb_attn_decode", "kb_attn_decode_workspace_bytes",
+            "kb_attn_strerror", "kb_attn_contract"} <= set(names)
+    lib = kb.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_contract_matches_header():
+    text = open(HEADER).read()
+    tile = int(re.search(r"#define KB_ATTN_KV_TILE (\d+)", text).group(1))
+    chunk = int(re.search(r"#define KB_ATTN_KV_CHUNK (\d+)", text).group(1))
+    c = kb.contract()
+    assert (c["kv_tile"], c["kv_chunk"]) == (tile, chunk) == (64, 1024)
+    kb.lib().kb_attn_contract(None, None, None)  # NULL outputs are allowed
+
+
+def test_strerror():
+    for code in (OK, INVALID, UNSUPPORTED, LENGTH, ALIGN, DEVICE, WORKSPACE, ALIAS, HIP, 12345):
+        assert kb.lib().kb_attn_strerror(code)
+
+
+@pytest.mark.parametrize("batch,kv_len,expect", [
+    (1, 1, 0), (1, 1024, 0), (16, 8192, 16 * 32 * 8 * 130 * 4), (4, 1025, 4 * 32 * 2 * 130 * 4),
+    (0, 100, 0), (1, 0, 0),
+])
+def test_workspace_bytes(batch, kv_len, expect):
+    assert kb.decode_workspace_bytes(batch, kv_len) == expect
+
+
+def prefill(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, batch=1, seq=16, hq=32, hkv=8, d=128, scale=SCALE)
+    a.update(kw)
+    return kb.lib().kb_attn_prefill(a["q"], a["k"], a["v"], a["o"], a["batch"], a["seq"], a["hq"], a["hkv"],
+                                    a["d"], a["scale"], None)
+
+
+def partitioned(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, batch=1, q_len=8, kv_len=16, cap=16, hq=32, hkv=8, d=128, scale=SCALE)
+    a.update(kw)
+    return kb.lib().kb_attn_partitioned(a["q"], a["k"], a["v"], a["o"], a["batch"], a["q_len"], a["kv_len"],
+                                        a["cap"], a["hq"], a["hkv"], a["d"], a["scale"], None)
+
+
+def decode(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, batch=1, kv_len=2048, cap=4096, hq=32, hkv=8, d=128, scale=SCALE, ws=W,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    return kb.lib().kb_attn_decode(a["q"], a["k"], a["v"], a["o"], a["batch"], a["kv_len"], a["cap"], a["hq"],
+                                   a["hkv"], a["d"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("call", [prefill, partitioned, decode])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(batch=0), INVALID), (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(hq=16), UNSUPPORTED), (dict(hq=32, hkv=4), UNSUPPORTED),
+    (dict(hkv=0), INVALID),
+    (dict(q=ctypes.c_void_p(Q.value + 2)), ALIGN), (dict(o=ctypes.c_void_p(O.value + 8)), ALIGN),
+    (dict(o=Q), ALIAS), (dict(o=K), ALIAS), (dict(o=V), ALIAS),
+])
+def test_rejected_before_launch(call, kw, expect):
+    assert call(**kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(q_len=0), dict(q_len=17), dict(kv_len=17), dict(cap=1 << 31, kv_len=1 << 31)])
+def test_partitioned_lengths(kw):
+    assert partitioned(**kw) == LENGTH
+
+
+@pytest.mark.parametrize("kw", [dict(kv_len=0), dict(kv_len=4097), dict(cap=(1 << 30) + 1)])
+def test_decode_lengths(kw):
+    assert decode(**kw) == LENGTH
+
+
+def test_prefill_length():
+    assert prefill(seq=0) == INVALID
+    assert prefill(seq=(1 << 30) + 1) == LENGTH
+
+
+def test_decode_workspace_checks():
+    need = kb.decode_workspace_bytes(1, 2048)
+    assert decode(ws=None) == WORKSPACE
+    assert decode(ws_bytes=need - 1) == WORKSPACE
+    assert decode(ws=ctypes.c_void_p(W.value + 4)) == ALIGN
+    assert decode(ws=O, ws_bytes=need) == ALIAS
+    assert decode(ws=ctypes.c_void_p(K.value + 64)) == ALIAS
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 32, 4, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kb.prefill(q, k, k)
+    with pytest.raises(ValueError):
+        kb.decode(q[:, :, :1].contiguous(), k, k)
