@@ -1,0 +1,126 @@
+"""Turn rocprofv3 output of bench.py into the short summaries kept in profiles/.
+
+The GPU runs (each command runs committed files only):
+  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline
+  rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
+  rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
+  rocprofv3 --pmc FETCH_SIZE -d <copy_fetch> -o run --output-format csv -- python3 bench.py --copy-probe
+  rocprofv3 --pmc WRITE_SIZE -d <copy_write> -o run --output-format csv -- python3 bench.py --copy-probe
+Then, on any host:
+  python bench_profile.py --stats <stats> --fetch <fetch> --write <write> \
+      --copy-fetch <copy_fetch> --copy-write <copy_write> --out profiles
+
+FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  Each is scaled by the
+factor that makes the plain 1 GiB copy read and write exactly 1 GiB.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+
+import bench
+
+COPY_BYTES = 1 << 30
+KERNELS = {
+    "prefill_kernel<false>": ("prefill_kernel_b16_s16384", "full causal prefill B=16 S=16384 (one launch per step)"),
+    "prefill_kernel<true>": ("prefill_kernel_partitioned_b16_16x1024",
+                             "partitioned forward, 16 launches of 1024 rows against the S=16384 cache"),
+    "decode_kernel": ("decode_kernel_b16_l8192", "decode split-KV at context 8192, B=16 (8 chunks)"),
+    "combine_kernel": ("combine_kernel_b16_l8192", "decode combine of 8 chunks, B=16"),
+}
+
+
+def find_csv(d: str, suffix: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def short(name: str):
+    for k in KERNELS:
+        if k in name:
+            return k
+    return None
+
+
+def per_dispatch(d: str):
+    out = {}
+    for r in csv.DictReader(open(find_csv(d, "counter_collection.csv"))):
+        out.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Dispatch_Id"]), int(r["Grid_Size"]), float(r["Counter_Value"]),
+             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
+
+
+def copy_factor(d: str) -> float:
+    vals = [v for name, rows in per_dispatch(d).items() if "copyBuffer" in name for (_, _, v, _) in rows]
+    return COPY_BYTES / 1024.0 / statistics.mean(vals)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    for a in ("stats", "fetch", "write", "copy_fetch", "copy_write", "out"):
+        ap.add_argument("--" + a.replace("_", "-"), required=True)
+    args = ap.parse_args()
+    f_fetch, f_write = copy_factor(args.copy_fetch), copy_factor(args.copy_write)
+    stats = {}
+    for r in csv.DictReader(open(find_csv(args.stats, "kernel_stats.csv"))):
+        k = short(r["Name"])
+        if k:
+            stats[k] = r
+    fetch, write = per_dispatch(args.fetch), per_dispatch(args.write)
+    src_hash = bench.kernel_source_hash()
+    os.makedirs(args.out, exist_ok=True)
+    for k, (fname, what) in KERNELS.items():
+        st = stats.get(k)
+        fr = [v for n, rows in fetch.items() if short(n) == k for v in rows]
+        wr = [v for n, rows in write.items() if short(n) == k for v in rows]
+        if not st or not fr or not wr:
+            continue
+        fetch_kib = statistics.mean(v for _, _, v, _ in fr)
+        write_kib = statistics.mean(v for _, _, v, _ in wr)
+        hbm = (fetch_kib * f_fetch + write_kib * f_write) * 1024.0
+        lines = [
+            f"# {k}: {what}",
+            f"kernel source hash: {src_hash}",
+            "",
+            "commands:",
+            "  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- "
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+            "  rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- "
+            "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+            "  rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- "
+            "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+            "  rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE ... -- python3 bench.py --copy-probe   (1 GiB copy)",
+            "  python bench_profile.py --stats <stats> --fetch <fetch> --write <write> "
+            "--copy-fetch <copy_fetch> --copy-write <copy_write> --out profiles",
+            "",
+            "kernel-trace --stats:",
+            f"  calls {st['Calls']}, average {float(st['AverageNs']) / 1e3:.1f} us, "
+            f"min {float(st['MinNs']) / 1e3:.1f} us, max {float(st['MaxNs']) / 1e3:.1f} us, "
+            f"{float(st['Percentage']):.2f} % of GPU time",
+            "",
+            "counters (per dispatch, mean over the profiled dispatches):",
+            f"  dispatches {len(fr)}, FETCH_SIZE {fetch_kib:.1f} KiB, WRITE_SIZE {write_kib:.1f} KiB",
+            f"  copy calibration: 1 GiB copy reads {COPY_BYTES / 1024 / f_fetch:.0f} KiB, "
+            f"writes {COPY_BYTES / 1024 / f_write:.0f} KiB -> factors fetch x{f_fetch:.3f}, write x{f_write:.3f}",
+            f"  HBM bytes per dispatch (scaled): {hbm:.4e}",
+        ]
+        with open(os.path.join(args.out, fname + ".txt"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        rec = {"kernel": k, "workload": what, "kernel_source_hash": src_hash, "fetch_kib": fetch_kib,
+               "write_kib": write_kib, "fetch_factor": f_fetch, "write_factor": f_write,
+               "hbm_bytes_per_launch": hbm, "avg_duration_us": float(st["AverageNs"]) / 1e3,
+               "calls_in_stats_run": int(st["Calls"])}
+        with open(os.path.join(args.out, fname + "_traffic.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(f"{k}: avg {rec['avg_duration_us']:.1f} us, HBM {hbm:.3e} B/launch")
+
+
+if __name__ == "__main__":
+    main()

@@ -33,30 +33,48 @@ struct PrefillArgs {
     uint16_t* o;
     int64_t q_len, kv_len, cap;
     int32_t batch, n_kv_heads;
-    int32_t qb_first, n_qb;  // 32-position blocks covered by the call
+    int32_t pb_first, n_pb;  // 64-position blocks covered by the call
     float c;                 // scale * log2(e), rounded once to fp32
 };
 
-// Workgroup = 4 waves = the 4 query heads of one KV head, on the 32 absolute
-// positions [32 qb, 32 qb + 32).  Every row of the block has its last visible
-// key in tile qb / 2, so all rows visit the same tiles 0..qb/2 and never a
-// tile that is fully masked for them.
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+constexpr int kPrefillWaves = 8;
+constexpr int kStages = 3;
+
+// Workgroup = 8 waves = the 4 query heads of one KV head x 2 halves of the 64
+// absolute positions [64 pb, 64 pb + 64).  Every row of the block has its last
+// visible key in tile pb, so all rows visit exactly the tiles 0..pb and never
+// a tile that is fully masked for them.  K/V tiles are shared by the 8 waves
+// through a 3-stage LDS ring filled by direct loads two tiles ahead.
+// kPartitioned = false is the full-sequence case (q_len == kv_len, row r at
+// position r); both instantiations run the same per-row arithmetic.
+template <bool kPartitioned>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nbg = a.batch * a.n_kv_heads;
     const int x = blockIdx.x;
-    const int bg = x % nbg;                               // same (b, g) -> same XCD when nbg % 8 == 0
-    const int qb = a.qb_first + a.n_qb - 1 - x / nbg;     // longest rows first
+    const int bg = x % nbg;                            // same (b, g) -> same XCD when nbg % 8 == 0
+    const int pb = a.pb_first + a.n_pb - 1 - x / nbg;  // longest rows first
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
     const int n_q_heads = kGroup * a.n_kv_heads;
-    const int head = kGroup * g + w;
+    const int head = kGroup * g + (w & 3);
     const int j = lane & 31, h = lane >> 5;
 
-    const int64_t off = a.kv_len - a.q_len;
-    const int64_t pos = (int64_t)qb * 32 + j;
+    const int64_t off = kPartitioned ? a.kv_len - a.q_len : 0;
+    const int64_t pos = (int64_t)pb * 64 + 32 * (w >> 2) + j;
     const int64_t r = pos - off;
     const bool active = r >= 0 && r < a.q_len;
+
+    const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
+    const uint16_t* kbase = a.k + kvoff;
+    const uint16_t* vbase = a.v + kvoff;
+    const int t_last = pb;
+
+    stage_issue(kbase, vbase, 0, a.kv_len, smem, smem + kKBytes, lane, w, kPrefillWaves);
+    if (t_last >= 1)
+        stage_issue(kbase, vbase, kTile, a.kv_len, smem + kTileBytes, smem + kTileBytes + kKBytes, lane, w,
+                    kPrefillWaves);
 
     bf16x8 qf[8];
     {
@@ -64,14 +82,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            const u32x4 x4 = active ? *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * h) : zero;
-            qf[st] = __builtin_bit_cast(bf16x8, x4);
+            const u32x4 x4 = *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * h);  // row valid either way
+            qf[st] = __builtin_bit_cast(bf16x8, active ? x4 : zero);
         }
     }
-    const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
-    const uint16_t* kbase = a.k + kvoff;
-    const uint16_t* vbase = a.v + kvoff;
-    const int t_last = qb >> 1;
 
     float M = -__builtin_inff(), L = 0.0f;
     f32x16 O[4];
@@ -84,14 +98,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
     bool have_total = false;
 
-    Stage st;
-    stage_load(st, kbase, vbase, 0, a.kv_len, tid);
-    stage_store(st, smem, smem + kKBytes, tid);
-    __syncthreads();
-
     for (int t = 0; t <= t_last; ++t) {
-        if (t < t_last) stage_load(st, kbase, vbase, (int64_t)(t + 1) * kTile, a.kv_len, tid);
-        const char* buf = smem + (t & 1) * kTileBytes;
+        // tile t has landed once at most the next tile's loads are pending
+        if (t + 1 <= t_last)
+            wait_vm<32 / kPrefillWaves>();
+        else
+            wait_vm<0>();
+        __syncthreads();
+        if (t + 2 <= t_last) {
+            char* nb = smem + ((t + 2) % kStages) * kTileBytes;
+            stage_issue(kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w,
+                        kPrefillWaves);
+        }
+        const char* buf = smem + (t % kStages) * kTileBytes;
         tile_step<4>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == t_last, a.c, m, l, acc, 0);
         if ((t % kTilesPerChunk) == kTilesPerChunk - 1 || t == t_last) {
             if (!have_total) {
@@ -116,11 +135,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int db = 0; db < 4; ++db) acc[db] = zero16();
         }
-        if (t < t_last) {
-            char* nbuf = smem + ((t + 1) & 1) * kTileBytes;
-            stage_store(st, nbuf, nbuf + kKBytes, tid);
-        }
-        __syncthreads();
     }
 
     if (active) {
@@ -152,12 +166,16 @@ struct DecodeArgs {
     float c;
 };
 
+constexpr int kDecodeWaves = 4;
+
 // Workgroup = 4 waves on one (batch, KV head, chunk).  The four query heads
 // sit in MFMA columns 0..3 (the other columns hold zeros).  Every wave computes
 // the scores of the tile; wave w accumulates the output rows d = 32w..32w+31.
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// The chunk's tiles stream through a 3-stage LDS ring two tiles ahead.
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int x = blockIdx.x;
     const int chunk = x % a.n_chunks;
     const int bg = x / a.n_chunks;
@@ -168,16 +186,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int head = kGroup * g + (active ? j : 0);
     const int64_t pos = a.kv_len - 1;
 
-    bf16x8 qf[8];
-    {
-        const uint16_t* qrow = a.q + ((int64_t)b * n_q_heads + head) * kHeadDim;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const u32x4 x4 = active ? *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * h) : zero;
-            qf[st] = __builtin_bit_cast(bf16x8, x4);
-        }
-    }
     const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
     const uint16_t* kbase = a.k + kvoff;
     const uint16_t* vbase = a.v + kvoff;
@@ -185,23 +193,37 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int t0 = chunk * kTilesPerChunk;
     const int t1 = min(t0 + kTilesPerChunk, n_tiles);
 
+    stage_issue(kbase, vbase, (int64_t)t0 * kTile, a.kv_len, smem, smem + kKBytes, lane, w, kDecodeWaves);
+    if (t0 + 1 < t1)
+        stage_issue(kbase, vbase, (int64_t)(t0 + 1) * kTile, a.kv_len, smem + kTileBytes,
+                    smem + kTileBytes + kKBytes, lane, w, kDecodeWaves);
+
+    bf16x8 qf[8];
+    {
+        const uint16_t* qrow = a.q + ((int64_t)b * n_q_heads + head) * kHeadDim;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const u32x4 x4 = *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * h);  // row valid either way
+            qf[st] = __builtin_bit_cast(bf16x8, active ? x4 : zero);
+        }
+    }
+
     float m = -__builtin_inff(), l = 0.0f;
     f32x16 acc[1];
     acc[0] = zero16();
-
-    Stage st;
-    stage_load(st, kbase, vbase, (int64_t)t0 * kTile, a.kv_len, tid);
-    stage_store(st, smem, smem + kKBytes, tid);
-    __syncthreads();
     for (int t = t0; t < t1; ++t) {
-        if (t + 1 < t1) stage_load(st, kbase, vbase, (int64_t)(t + 1) * kTile, a.kv_len, tid);
-        const char* buf = smem + ((t - t0) & 1) * kTileBytes;
-        tile_step<1>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == n_tiles - 1, a.c, m, l, acc, w);
-        if (t + 1 < t1) {
-            char* nbuf = smem + ((t + 1 - t0) & 1) * kTileBytes;
-            stage_store(st, nbuf, nbuf + kKBytes, tid);
-        }
+        if (t + 1 < t1)
+            wait_vm<32 / kDecodeWaves>();
+        else
+            wait_vm<0>();
         __syncthreads();
+        if (t + 2 < t1) {
+            char* nb = smem + ((t + 2 - t0) % kStages) * kTileBytes;
+            stage_issue(kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w, kDecodeWaves);
+        }
+        const char* buf = smem + ((t - t0) % kStages) * kTileBytes;
+        tile_step<1>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == n_tiles - 1, a.c, m, l, acc, w);
     }
 
     if (!active) return;
@@ -318,8 +340,8 @@ int check_device(std::initializer_list<const void*> ptrs) {
 
 int64_t n_chunks_of(int64_t kv_len) { return (kv_len + kChunk - 1) / kChunk; }
 
-int launch_prefill(const void* q, const void* k, const void* v, void* o, int64_t batch, int64_t q_len,
-                   int64_t kv_len, int64_t cap, int32_t n_kv_heads, float scale, hipStream_t stream) {
+int launch_prefill(bool partitioned, const void* q, const void* k, const void* v, void* o, int64_t batch,
+                   int64_t q_len, int64_t kv_len, int64_t cap, int32_t n_kv_heads, float scale, hipStream_t stream) {
     PrefillArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
@@ -330,13 +352,16 @@ int launch_prefill(const void* q, const void* k, const void* v, void* o, int64_t
     a.cap = cap;
     a.batch = (int32_t)batch;
     a.n_kv_heads = n_kv_heads;
-    const int64_t first = (kv_len - q_len) / 32, last = (kv_len - 1) / 32;
-    a.qb_first = (int32_t)first;
-    a.n_qb = (int32_t)(last - first + 1);
+    const int64_t first = (kv_len - q_len) / 64, last = (kv_len - 1) / 64;
+    a.pb_first = (int32_t)first;
+    a.n_pb = (int32_t)(last - first + 1);
     a.c = contract_c(scale);
-    const int64_t grid = (int64_t)a.n_qb * batch * n_kv_heads;
+    const int64_t grid = (int64_t)a.n_pb * batch * n_kv_heads;
     if (grid > INT32_MAX) return KB_ATTN_ERR_LENGTH;
-    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    if (!partitioned)
+        hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(64 * kPrefillWaves), 0, stream, a);
+    else
+        hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(64 * kPrefillWaves), 0, stream, a);
     return hipGetLastError() == hipSuccess ? KB_ATTN_OK : KB_ATTN_ERR_HIP;
 }
 
@@ -360,7 +385,7 @@ int kb_attn_prefill(const void* q, const void* k, const void* v, void* o, int64_
         ranges_overlap(o, qbytes, v, kvbytes))
         return KB_ATTN_ERR_ALIAS;
     if (int rc = check_device({q, k, v, o})) return rc;
-    return launch_prefill(q, k, v, o, batch, seq_len, seq_len, seq_len, n_kv_heads, scale, stream);
+    return launch_prefill(false, q, k, v, o, batch, seq_len, seq_len, seq_len, n_kv_heads, scale, stream);
 }
 
 int kb_attn_partitioned(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch,
@@ -378,7 +403,8 @@ int kb_attn_partitioned(const void* q, const void* k_cache, const void* v_cache,
         ranges_overlap(o, qbytes, v_cache, kvbytes))
         return KB_ATTN_ERR_ALIAS;
     if (int rc = check_device({q, k_cache, v_cache, o})) return rc;
-    return launch_prefill(q, k_cache, v_cache, o, batch, q_len, kv_len, kv_capacity, n_kv_heads, scale, stream);
+    return launch_prefill(true, q, k_cache, v_cache, o, batch, q_len, kv_len, kv_capacity, n_kv_heads, scale,
+                          stream);
 }
 
 size_t kb_attn_decode_workspace_bytes(int64_t batch, int64_t kv_len, int32_t n_q_heads, int32_t head_dim) {
@@ -426,7 +452,7 @@ int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
     a.c = contract_c(scale);
     const int64_t grid = batch * n_kv_heads * nc;
     if (grid > INT32_MAX || rows > INT32_MAX) return KB_ATTN_ERR_LENGTH;
-    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)grid), dim3(64 * kDecodeWaves), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
     if (nc > 1) {
         CombineArgs cmb;

@@ -49,36 +49,105 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// LDS tile layout (one K/V tile of 64 keys):
-//   K   row-major [64 keys][128 d], 256 B per key row, 16-byte chunk c of row
-//       r stored at chunk position c ^ (r & 15)  (conflict-free A reads)
-//   V^T [128 d][64 keys in MFMA slot order], 128 B per d row, chunk c of row d
-//       at chunk position c ^ ((d >> 1) & 7)
-// Slot order of V^T: chunk 2*(2*kb+u)+h holds, in order, keys
-//   32kb+16u+4h+{0,1,2,3}, 32kb+16u+8+4h+{0,1,2,3}
-// which is the key order of the P^T operand taken straight from the S^T
-// accumulator (lane half h holds accumulator rows 8b+4h+e).
+// LDS tile layout (one K/V tile of 64 keys), both row-major, 256 B per key:
+//   K  16-byte chunk c of key row r at chunk position c ^ (r & 15)
+//      (the A-operand reads, 16 rows x one chunk per 16 lanes, hit 16
+//      distinct bank groups)
+//   V  16-byte chunk c of key row r at chunk position c ^ ((r & 3) << 2)
+//      (the transposing reads touch 4 rows x 4 chunks per 32 lanes)
+// Tiles are filled by global_load_lds_dwordx4: lane L of an instruction
+// lands at the instruction's LDS base + 16 L, so each lane fetches the global
+// chunk that belongs at its LDS position.  Keys at or beyond kv_len read the
+// (valid) row kv_len - 1 instead: those keys are masked (K) or weighted by
+// P = 0 (V), so only finite values ever enter the products.
 // ---------------------------------------------------------------------------
 constexpr int kKBytes = kTile * kHeadDim * 2;
 constexpr int kVBytes = kTile * kHeadDim * 2;
 constexpr int kTileBytes = kKBytes + kVBytes;
 
-__device__ __forceinline__ int k_lds_off(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 
-__device__ __forceinline__ int vt_lds_off(int d, int chunk) { return d * 128 + ((chunk ^ ((d >> 1) & 7)) << 4); }
-
-// byte offset, inside its V^T row, of key kk (0..63) of the tile
-__device__ __forceinline__ int vt_key_chunk(int kk) {
-    const int kb = kk >> 5, u = (kk >> 4) & 1, h = (kk >> 2) & 1;
-    return 2 * (2 * kb + u) + h;
+// Issue this wave's share of the 32 one-KiB direct loads of a tile:
+// instructions i = wave, wave + n_waves, ... (0..15 fill K rows 4i..4i+3,
+// 16..31 fill V rows 4(i-16)..+3).  The loads are issued as inline assembly
+// so that the compiler does not serialise every later LDS read behind them;
+// completion is tracked explicitly with wait_vm() before the workgroup
+// barrier that publishes the tile.
+__device__ __forceinline__ void stage_issue(const uint16_t* kbase, const uint16_t* vbase, int64_t key0,
+                                            int64_t kv_len, char* sK, char* sV, int lane, int wave,
+                                            int n_waves) {
+    for (int i = wave; i < 32; i += n_waves) {
+        const bool is_v = i >= 16;
+        const int row = 4 * (i & 15) + (lane >> 4);
+        const int pc = lane & 15;
+        const int c = pc ^ (is_v ? v_swz(row) : k_swz(row));
+        int64_t key = key0 + row;
+        key = key < kv_len ? key : kv_len - 1;
+        const uint16_t* src = (is_v ? vbase : kbase) + key * kHeadDim + c * 8;
+        const char* dst = (is_v ? sV : sK) + 1024 * (i & 15);
+        const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+        uint32_t saved_m0;
+        // M0 is saved and restored around the load; s_nop covers the one
+        // wait state required between an M0 write and an LDS-DMA load
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, off\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved_m0)
+            : "v"(src), "s"(lds_base)
+            : "memory");
+    }
 }
-__device__ __forceinline__ int vt_key_byte(int kk) {
-    const int a = (kk >> 3) & 1, e = kk & 3;
-    return (4 * a + e) * 2;
+
+// Number of direct loads stage_issue gives one wave.
+__device__ __forceinline__ int stage_count(int wave, int n_waves) { return (32 - wave + n_waves - 1) / n_waves; }
+
+// Wait until at most n of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 __device__ __forceinline__ bf16x8 lds_read16(const char* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// A operand of S^T = K Q^T for key block kb, k-step st:
+// lane (key j, half h) holds K[32kb + j][16st + 8h .. +7]
+__device__ __forceinline__ bf16x8 k_frag(const char* sK, int kb, int st, int lane) {
+    const int row = 32 * kb + (lane & 31);
+    const int c = 2 * st + (lane >> 5);
+    return lds_read16(sK + row * 256 + ((c ^ k_swz(row)) << 4));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// A operand of O^T += V^T P^T for key step (kb, u) and d block dblk:
+// lane (d = 32 dblk + j, half h) holds, in slot order,
+//   V[K0 + 4h + {0..3}][d], V[K0 + 8 + 4h + {0..3}][d]      with K0 = 32kb + 16u
+// read with two ds_read_b64_tr_b16.  Within each 16-lane group, lane i of the
+// result takes element (i & 3) of the 8-byte blocks read by lanes 4n + (i >> 2)
+// (n = 0..3), so lane L = 16 g + 4 n + jj reads V[K0 + 4 (g >> 1) + n][32 dblk +
+// 16 (g & 1) + 4 jj .. +3].
+__device__ __forceinline__ bf16x8 vt_frag(const char* sV, int kb, int u, int dblk, int lane) {
+    const int g = lane >> 4, n = (lane >> 2) & 3, jj = lane & 3;
+    const int row0 = 32 * kb + 16 * u + 4 * (g >> 1) + n;
+    const int d = 32 * dblk + 16 * (g & 1) + 4 * jj;
+    const int c = d >> 3, half = (d & 4) << 1;  // byte offset 0 or 8 inside the chunk
+    const int row1 = row0 + 8;
+    const char* p0 = sV + row0 * 256 + ((c ^ v_swz(row0)) << 4) + half;
+    const char* p1 = sV + row1 * 256 + ((c ^ v_swz(row1)) << 4) + half;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 all = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, all);
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -95,60 +164,6 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 
 // ---------------------------------------------------------------------------
-// Staging of one tile from global memory into LDS by a 256-thread workgroup.
-// Keys at or beyond kv_len read as zero (never loaded).
-// ---------------------------------------------------------------------------
-struct Stage {
-    u32x4 k[4];
-    u32x4 v[2][2];
-};
-
-__device__ __forceinline__ void stage_load(Stage& s, const uint16_t* kbase, const uint16_t* vbase,
-                                           int64_t key0, int64_t kv_len, int tid) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int u = tid + 256 * i;
-        const int row = u >> 4, c = u & 15;
-        const int64_t key = key0 + row;
-        s.k[i] = key < kv_len ? *reinterpret_cast<const u32x4*>(kbase + key * kHeadDim + c * 8) : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = tid + 256 * i;
-        const int dg = u >> 5, kp = u & 31;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int64_t key = key0 + 2 * kp + e;
-            s.v[i][e] = key < kv_len ? *reinterpret_cast<const u32x4*>(vbase + key * kHeadDim + dg * 8) : zero;
-        }
-    }
-}
-
-__device__ __forceinline__ void stage_store(const Stage& s, char* sK, char* sVt, int tid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int u = tid + 256 * i;
-        const int row = u >> 4, c = u & 15;
-        *reinterpret_cast<u32x4*>(sK + k_lds_off(row, c)) = s.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = tid + 256 * i;
-        const int dg = u >> 5, kp = u & 31;
-        const int kk = 2 * kp;
-        const int chunk = vt_key_chunk(kk), byte = vt_key_byte(kk);
-#pragma unroll
-        for (int d8 = 0; d8 < 8; ++d8) {
-            const int word = d8 >> 1, sh = (d8 & 1) * 16;
-            const uint32_t lo = (s.v[i][0][word] >> sh) & 0xFFFFu;
-            const uint32_t hi = (s.v[i][1][word] >> sh) & 0xFFFFu;
-            *reinterpret_cast<uint32_t*>(sVt + vt_lds_off(dg * 8 + d8, chunk) + byte) = lo | (hi << 16);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // One tile of the online softmax for the 32 query columns of a wave.
 // Lane l owns query column j = l & 31; lane half h = l >> 5.
 //   qf[st]  : B operand of k-step st: Q[query j][16st + 8h .. 16st + 8h + 7]
@@ -157,15 +172,15 @@ __device__ __forceinline__ void stage_store(const Stage& s, char* sK, char* sVt,
 //   o[db]   : O^T accumulators for d rows 32*(dblk0+db) .. +31 of column j
 // ---------------------------------------------------------------------------
 template <int NDB>
-__device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sVt, int lane,
+__device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
                                           int64_t key0, int64_t pos, bool mask, float c, float& m, float& l,
                                           f32x16 (&o)[NDB], int dblk0) {
     const int j = lane & 31, h = lane >> 5;
     f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-        const bf16x8 k0 = lds_read16(sK + k_lds_off(j, 2 * st + h));
-        const bf16x8 k1 = lds_read16(sK + k_lds_off(32 + j, 2 * st + h));
+        const bf16x8 k0 = k_frag(sK, 0, st, lane);
+        const bf16x8 k1 = k_frag(sK, 1, st, lane);
         s0 = mfma(k0, qf[st], s0);
         s1 = mfma(k1, qf[st], s1);
     }
@@ -213,10 +228,14 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
     const float ls = w[0] + __shfl_xor(w[0], 32);
     l = __builtin_fmaf(l, a, ls);
 
+    // o * 1 == o exactly, so skipping the rescale when no column of the wave
+    // changed its maximum leaves every bit as it is
+    if (__builtin_amdgcn_ballot_w64(a != 1.0f) != 0) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] = o[db][v] * a;
+            for (int v = 0; v < 16; ++v) o[db][v] = o[db][v] * a;
+        }
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -224,7 +243,7 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const bf16x8 vf = lds_read16(sVt + vt_lds_off(32 * (dblk0 + db) + j, 2 * (2 * kb + u) + h));
+                const bf16x8 vf = vt_frag(sV, kb, u, dblk0 + db, lane);
                 o[db] = mfma(vf, pf[kb][u], o[db]);
             }
         }
