@@ -87,9 +87,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
         }
     }
 
-    float M = -__builtin_inff(), L = 0.0f;
+    // running maxima are kept in log2 units (max * c)
+    float Mc = -__builtin_inff(), L = 0.0f;
     f32x16 O[4];
-    float m = -__builtin_inff(), l = 0.0f;
+    float mc = -__builtin_inff(), l = 0.0f;
     f32x16 acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
     for (int t = 0; t <= t_last; ++t) {
         // tile t has landed once at most the next tile's loads are pending
         if (t + 1 <= t_last)
-            wait_vm<32 / kPrefillWaves>();
+            wait_vm<kTileLoads / kPrefillWaves>();
         else
             wait_vm<0>();
         __syncthreads();
@@ -111,26 +112,26 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
                         kPrefillWaves);
         }
         const char* buf = smem + (t % kStages) * kTileBytes;
-        tile_step<4>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == t_last, a.c, m, l, acc, 0);
+        tile_step<4>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == t_last, a.c, mc, l, acc, 0);
         if ((t % kTilesPerChunk) == kTilesPerChunk - 1 || t == t_last) {
             if (!have_total) {
-                M = m;
+                Mc = mc;
                 L = l;
 #pragma unroll
                 for (int db = 0; db < 4; ++db) O[db] = acc[db];
                 have_total = true;
             } else {
-                float Mn, A, B;
-                fold_scalars(M, m, a.c, Mn, A, B);
+                float Mcn, A, B;
+                fold_scalars(Mc, mc, Mcn, A, B);
                 L = __builtin_fmaf(L, A, l * B);
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) O[db][v] = fold_value(O[db][v], A, acc[db][v], B);
                 }
-                M = Mn;
+                Mc = Mcn;
             }
-            m = -__builtin_inff();
+            mc = -__builtin_inff();
             l = 0.0f;
 #pragma unroll
             for (int db = 0; db < 4; ++db) acc[db] = zero16();
@@ -160,7 +161,7 @@ struct DecodeArgs {
     const uint16_t* v;
     uint16_t* o;
     float* ws_o;   // [batch * n_q_heads * n_chunks][128]
-    float* ws_ml;  // [batch * n_q_heads * n_chunks][2]
+    float* ws_ml;  // [batch * n_q_heads * n_chunks][2]: (max * c, sum)
     int64_t kv_len, cap;
     int32_t batch, n_kv_heads, n_chunks;
     float c;
@@ -209,12 +210,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         }
     }
 
-    float m = -__builtin_inff(), l = 0.0f;
+    float mc = -__builtin_inff(), l = 0.0f;  // max in log2 units
     f32x16 acc[1];
     acc[0] = zero16();
     for (int t = t0; t < t1; ++t) {
         if (t + 1 < t1)
-            wait_vm<32 / kDecodeWaves>();
+            wait_vm<kTileLoads / kDecodeWaves>();
         else
             wait_vm<0>();
         __syncthreads();
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
             stage_issue(kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w, kDecodeWaves);
         }
         const char* buf = smem + ((t - t0) % kStages) * kTileBytes;
-        tile_step<1>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == n_tiles - 1, a.c, m, l, acc, w);
+        tile_step<1>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == n_tiles - 1, a.c, mc, l, acc, w);
     }
 
     if (!active) return;
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         *reinterpret_cast<float4*>(po + 32 * w + 8 * b4 + 4 * h) = f;
     }
     if (w == 0 && h == 0) {
-        a.ws_ml[prow * 2 + 0] = m;
+        a.ws_ml[prow * 2 + 0] = mc;
         a.ws_ml[prow * 2 + 1] = l;
     }
 }
@@ -273,18 +274,18 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     const int64_t row = blockIdx.x;
     const int d = threadIdx.x;
     const int64_t base = row * a.n_chunks;
-    float M = a.ws_ml[base * 2 + 0];
+    float Mc = a.ws_ml[base * 2 + 0];
     float L = a.ws_ml[base * 2 + 1];
     float O = a.ws_o[base * kHeadDim + d];
     for (int k = 1; k < a.n_chunks; ++k) {
-        const float m = a.ws_ml[(base + k) * 2 + 0];
+        const float mc = a.ws_ml[(base + k) * 2 + 0];
         const float l = a.ws_ml[(base + k) * 2 + 1];
         const float o = a.ws_o[(base + k) * kHeadDim + d];
-        float Mn, A, B;
-        fold_scalars(M, m, a.c, Mn, A, B);
+        float Mcn, A, B;
+        fold_scalars(Mc, mc, Mcn, A, B);
         L = __builtin_fmaf(L, A, l * B);
         O = fold_value(O, A, o, B);
-        M = Mn;
+        Mc = Mcn;
     }
     a.o[row * kHeadDim + d] = finalize(O, L);
 }

@@ -14,19 +14,19 @@
 //             S^T[key][query] = K[key][:] . Q^T[:][query]     (A = K, B = Q^T)
 //             O^T[d][query]  += V^T[d][keys] . P^T[keys][query] (A = V^T, B = P^T)
 //           one query per MFMA column; column position never changes bits.
-//   per row, per tile, in order:
+//   per row, per tile, in order (running state mc = reference max * c, l, o):
 //     s_j   = MFMA chain over d in k-steps 0..7 (step st covers d 16st..16st+15)
 //     s_j   = -inf where key j > pos                  (select)
-//     mt    = max_j s_j
-//     m'    = max(m, mt);  nc = -(m' * c)            with c = fp32(scale * log2 e)
-//     a     = (m' == m) ? 1 : exp2(fma(m, c, nc))
-//     p_j   = exp2(fma(s_j, c, nc));  P_j = bf16_rne(p_j)
-//     l     = fma(l, a, tree_sum(P))                  (fixed tree, see tile_step)
+//     mtc   = (max_j s_j) * c                         with c = fp32(scale * log2 e)
+//     grow  = mtc - mc > 8;  mc' = grow ? mtc : mc;  a = grow ? exp2(mc - mc') : 1
+//     p_j   = exp2(fma(s_j, c, -mc'));  P_j = bf16_rne(p_j)   (P_j <= 2^8)
+//     l     = fma(l, a, sum(P))   sum: per 16-key step, a chain of 4 bf16 dot2
+//             with (1, 1); then ((k0u0 + k0u1) + (k1u0 + k1u1)) + partner half
 //     o     = o * a;  o = MFMA chain over the tile's 4 key steps in order
-//     m     = m'
+//     mc    = mc'
 //   per chunk, in chunk order (first chunk is copied, the rest folded):
-//     M' = max(M, m); nc = -(M' c); A = (M' == M) ? 1 : exp2(fma(M, c, nc))
-//     B  = (M' == m) ? 1 : exp2(fma(m, c, nc)); L = fma(L, A, l B); O = fma(O, A, o B)
+//     Mc' = max(Mc, mc); A = (Mc' == Mc) ? 1 : exp2(Mc - Mc')
+//     B   = (Mc' == mc) ? 1 : exp2(mc - Mc'); L = fma(L, A, l B); O = fma(O, A, o B)
 //   out = bf16_rne(O / L)  (IEEE division)
 //
 // Compile every kernel of the library in one translation unit with
@@ -64,6 +64,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kKBytes = kTile * kHeadDim * 2;
 constexpr int kVBytes = kTile * kHeadDim * 2;
 constexpr int kTileBytes = kKBytes + kVBytes;
+constexpr int kTileLoads = kTileBytes / 1024;  // 32 one-KiB direct loads
 
 __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
@@ -77,7 +78,7 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 __device__ __forceinline__ void stage_issue(const uint16_t* kbase, const uint16_t* vbase, int64_t key0,
                                             int64_t kv_len, char* sK, char* sV, int lane, int wave,
                                             int n_waves) {
-    for (int i = wave; i < 32; i += n_waves) {
+    for (int i = wave; i < kTileLoads; i += n_waves) {
         const bool is_v = i >= 16;
         const int row = 4 * (i & 15) + (lane >> 4);
         const int pc = lane & 15;
@@ -103,10 +104,7 @@ __device__ __forceinline__ void stage_issue(const uint16_t* kbase, const uint16_
     }
 }
 
-// Number of direct loads stage_issue gives one wave.
-__device__ __forceinline__ int stage_count(int wave, int n_waves) { return (32 - wave + n_waves - 1) / n_waves; }
-
-// Wait until at most n of this wave's vector-memory operations are pending.
+// Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -169,14 +167,18 @@ __device__ __forceinline__ f32x16 zero16() {
 //   qf[st]  : B operand of k-step st: Q[query j][16st + 8h .. 16st + 8h + 7]
 //   key0    : absolute index of the tile's first key
 //   pos     : the column's position (keys > pos are masked) -- used when mask
+//   mc, l   : running max in log2 units (max * c) and running sum
 //   o[db]   : O^T accumulators for d rows 32*(dblk0+db) .. +31 of column j
 // ---------------------------------------------------------------------------
-template <int NDB>
-__device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
-                                          int64_t key0, int64_t pos, bool mask, float c, float& m, float& l,
-                                          f32x16 (&o)[NDB], int dblk0) {
-    const int j = lane & 31, h = lane >> 5;
-    f32x16 s0 = zero16(), s1 = zero16();
+constexpr float kLazyTau = 8.0f;  // the reference max moves only when the tile max exceeds it by > 8 (log2)
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Scores of one tile: S^T for key blocks 0 (s0) and 1 (s1).
+__device__ __forceinline__ void qk_tile(const bf16x8 (&qf)[8], const char* sK, int lane, f32x16& s0, f32x16& s1) {
+    s0 = zero16();
+    s1 = zero16();
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
         const bf16x8 k0 = k_frag(sK, 0, st, lane);
@@ -184,6 +186,14 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
         s0 = mfma(k0, qf[st], s0);
         s1 = mfma(k1, qf[st], s1);
     }
+}
+
+// Mask, online-softmax update and P V of one tile whose scores are s0, s1.
+template <int NDB>
+__device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char* sV, int lane, int64_t key0,
+                                                int64_t pos, bool mask, float c, float& mc, float& l,
+                                                f32x16 (&o)[NDB], int dblk0) {
+    const int h = lane >> 5;
     if (mask) {
         const float ninf = -__builtin_inff();
 #pragma unroll
@@ -193,44 +203,51 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
             s1[v] = kk + 32 > pos ? ninf : s1[v];
         }
     }
-    float mt = s0[0];
+    float mt = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mt = fmaxf(mt, s0[v]);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s1[v]);
+    for (int v = 1; v < 16; ++v) mt = fmaxf(mt, fmaxf(s0[v], s1[v]));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
 
-    const float mn = fmaxf(m, mt);
-    const float nc = -(mn * c);
-    const float a = (mn == m) ? 1.0f : exp2_hw(__builtin_fmaf(m, c, nc));
+    // lazy reference max: keep mc while the tile max stays within kLazyTau
+    const float mtc = mt * c;
+    const bool grow = (mtc - mc) > kLazyTau;
+    const float mcn = grow ? mtc : mc;
+    const float a = grow ? exp2_hw(mc - mcn) : 1.0f;
+    const float nmc = -mcn;
 
     bf16x8 pf[2][2];
-    float w[32];
+    float part[2][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const __bf16 p0 = (__bf16)exp2_hw(__builtin_fmaf(s0[8 * u + e], c, nc));
-            const __bf16 p1 = (__bf16)exp2_hw(__builtin_fmaf(s1[8 * u + e], c, nc));
-            pf[0][u][e] = p0;
-            pf[1][u][e] = p1;
-            w[8 * u + e] = (float)p0;
-            w[16 + 8 * u + e] = (float)p1;
+        for (int u = 0; u < 2; ++u) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float x0 = kb ? s1[8 * u + e] : s0[8 * u + e];
+                const float x1 = kb ? s1[8 * u + e + 1] : s0[8 * u + e + 1];
+                f32x2 pp;
+                pp[0] = exp2_hw(__builtin_fmaf(x0, c, nmc));
+                pp[1] = exp2_hw(__builtin_fmaf(x1, c, nmc));
+                const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+                pf[kb][u][e] = pb[0];
+                pf[kb][u][e + 1] = pb[1];
+                const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+                acc = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, acc, false);
+            }
+            part[kb][u] = acc;
         }
     }
-    // fixed pairwise tree over the 32 slots (index 16*kb + 8u + e), then the
-    // partner lane's half: x + y == y + x, so both halves get the same bits
-#pragma unroll
-    for (int stride = 1; stride < 32; stride *= 2) {
-#pragma unroll
-        for (int i = 0; i < 32; i += 2 * stride) w[i] = w[i] + w[i + stride];
-    }
-    const float ls = w[0] + __shfl_xor(w[0], 32);
+    // fixed tree: each (kb, u) slot group chains its 4 pairs, then
+    // ((00 + 01) + (10 + 11)), then the partner lane's half: x + y == y + x,
+    // so both halves of a column get the same bits
+    const float ls_half = (part[0][0] + part[0][1]) + (part[1][0] + part[1][1]);
+    const float ls = ls_half + __shfl_xor(ls_half, 32);
     l = __builtin_fmaf(l, a, ls);
 
     // o * 1 == o exactly, so skipping the rescale when no column of the wave
-    // changed its maximum leaves every bit as it is
-    if (__builtin_amdgcn_ballot_w64(a != 1.0f) != 0) {
+    // moved its reference max leaves every bit as it is
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -248,15 +265,24 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
             }
         }
     }
-    m = mn;
+    mc = mcn;
 }
 
-// Fold weights of one chunk into the running total (scalars of one column).
-__device__ __forceinline__ void fold_scalars(float M, float m, float c, float& Mn, float& A, float& B) {
-    Mn = fmaxf(M, m);
-    const float nc = -(Mn * c);
-    A = (Mn == M) ? 1.0f : exp2_hw(__builtin_fmaf(M, c, nc));
-    B = (Mn == m) ? 1.0f : exp2_hw(__builtin_fmaf(m, c, nc));
+template <int NDB>
+__device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
+                                          int64_t key0, int64_t pos, bool mask, float c, float& mc, float& l,
+                                          f32x16 (&o)[NDB], int dblk0) {
+    f32x16 s0, s1;
+    qk_tile(qf, sK, lane, s0, s1);
+    softmax_pv_tile<NDB>(s0, s1, sV, lane, key0, pos, mask, c, mc, l, o, dblk0);
+}
+
+// Fold weights of one chunk into the running total (scalars of one column,
+// maxima in log2 units).
+__device__ __forceinline__ void fold_scalars(float Mc, float mc, float& Mcn, float& A, float& B) {
+    Mcn = fmaxf(Mc, mc);
+    A = (Mcn == Mc) ? 1.0f : exp2_hw(Mc - Mcn);
+    B = (Mcn == mc) ? 1.0f : exp2_hw(mc - Mcn);
 }
 
 __device__ __forceinline__ float fold_value(float O, float A, float o, float B) {
