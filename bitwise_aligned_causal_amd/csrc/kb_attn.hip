@@ -99,8 +99,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
     }
     bool have_total = false;
 
-    for (int t = 0; t <= t_last; ++t) {
-        // tile t has landed once at most the next tile's loads are pending
+    // Wait for this wave's loads of tile t, publish it to the workgroup, then
+    // start the loads of tile t + 2 into the stage nobody reads any more.
+    auto publish = [&](int t) {
         if (t + 1 <= t_last)
             wait_vm<kTileLoads / kPrefillWaves>();
         else
@@ -111,31 +112,44 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
             stage_issue(kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w,
                         kPrefillWaves);
         }
-        const char* buf = smem + (t % kStages) * kTileBytes;
-        tile_step<4>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == t_last, a.c, mc, l, acc, 0);
-        if ((t % kTilesPerChunk) == kTilesPerChunk - 1 || t == t_last) {
-            if (!have_total) {
-                Mc = mc;
-                L = l;
+    };
+    auto close_chunk = [&]() {
+        if (!have_total) {
+            Mc = mc;
+            L = l;
 #pragma unroll
-                for (int db = 0; db < 4; ++db) O[db] = acc[db];
-                have_total = true;
-            } else {
-                float Mcn, A, B;
-                fold_scalars(Mc, mc, Mcn, A, B);
-                L = __builtin_fmaf(L, A, l * B);
+            for (int db = 0; db < 4; ++db) O[db] = acc[db];
+            have_total = true;
+        } else {
+            float Mcn, A, B;
+            fold_scalars(Mc, mc, Mcn, A, B);
+            L = __builtin_fmaf(L, A, l * B);
 #pragma unroll
-                for (int db = 0; db < 4; ++db) {
+            for (int db = 0; db < 4; ++db) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) O[db][v] = fold_value(O[db][v], A, acc[db][v], B);
-                }
-                Mc = Mcn;
+                for (int v = 0; v < 16; ++v) O[db][v] = fold_value(O[db][v], A, acc[db][v], B);
             }
-            mc = -__builtin_inff();
-            l = 0.0f;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) acc[db] = zero16();
+            Mc = Mcn;
         }
+        mc = -__builtin_inff();
+        l = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] = zero16();
+    };
+
+    // tiles below the diagonal: every key visible to every row
+    for (int t = 0; t < t_last; ++t) {
+        publish(t);
+        const char* buf = smem + (t % kStages) * kTileBytes;
+        tile_step<4, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, a.c, mc, l, acc, 0);
+        if ((t % kTilesPerChunk) == kTilesPerChunk - 1) close_chunk();
+    }
+    // the diagonal tile t_last holds keys beyond some rows' positions
+    {
+        publish(t_last);
+        const char* buf = smem + (t_last % kStages) * kTileBytes;
+        tile_step<4, true>(qf, buf, buf + kKBytes, lane, (int64_t)t_last * kTile, pos, a.c, mc, l, acc, 0);
+        close_chunk();
     }
 
     if (active) {
@@ -224,7 +238,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
             stage_issue(kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w, kDecodeWaves);
         }
         const char* buf = smem + ((t - t0) % kStages) * kTileBytes;
-        tile_step<1>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, t == n_tiles - 1, a.c, mc, l, acc, w);
+        // only the context's last tile can hold keys beyond kv_len - 1
+        if (t < n_tiles - 1)
+            tile_step<1, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, a.c, mc, l, acc, w);
+        else
+            tile_step<1, true>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, a.c, mc, l, acc, w);
     }
 
     if (!active) return;

@@ -21,7 +21,8 @@
 //     grow  = mtc - mc > 8;  mc' = grow ? mtc : mc;  a = grow ? exp2(mc - mc') : 1
 //     p_j   = exp2(fma(s_j, c, -mc'));  P_j = bf16_rne(p_j)   (P_j <= 2^8)
 //     l     = fma(l, a, sum(P))   sum: per 16-key step, a chain of 4 bf16 dot2
-//             with (1, 1); then ((k0u0 + k0u1) + (k1u0 + k1u1)) + partner half
+//             with (1, 1); then ((k0u0 + k0u1) + (k1u0 + k1u1)) per lane half,
+//             then (low half + high half)
 //     o     = o * a;  o = MFMA chain over the tile's 4 key steps in order
 //     mc    = mc'
 //   per chunk, in chunk order (first chunk is copied, the rest folded):
@@ -148,6 +149,25 @@ __device__ __forceinline__ bf16x8 vt_frag(const char* sV, int kb, int u, int dbl
     return __builtin_bit_cast(bf16x8, all);
 }
 
+// Combine a value with the one held by the lane 32 apart (the other half of
+// the same MFMA column), with v_permlane32_swap: after the swap one copy holds
+// the low half's value in every lane and the other the high half's, so every
+// lane evaluates op(low, high) with the same operand order.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __builtin_bit_cast(float, (unsigned)r[0]);
+    hi = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// max of three floats (exact; written as one instruction so that no
+// canonicalising moves are inserted for MFMA results)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -186,15 +206,23 @@ __device__ __forceinline__ void qk_tile(const bf16x8 (&qf)[8], const char* sK, i
         s0 = mfma(k0, qf[st], s0);
         s1 = mfma(k1, qf[st], s1);
     }
+    // schedule: 8 fragment reads ahead, then 2 MFMAs per 2 reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
 // Mask, online-softmax update and P V of one tile whose scores are s0, s1.
-template <int NDB>
+template <int NDB, bool kMask>
 __device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char* sV, int lane, int64_t key0,
-                                                int64_t pos, bool mask, float c, float& mc, float& l,
-                                                f32x16 (&o)[NDB], int dblk0) {
+                                                int64_t pos, float c, float& mc, float& l, f32x16 (&o)[NDB],
+                                                int dblk0) {
     const int h = lane >> 5;
-    if (mask) {
+    if (kMask) {
         const float ninf = -__builtin_inff();
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -205,8 +233,12 @@ __device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char
     }
     float mt = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mt = fmaxf(mt, fmaxf(s0[v], s1[v]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    for (int v = 1; v < 16; ++v) mt = max3(mt, s0[v], s1[v]);
+    {
+        float lo, hi;
+        halves(mt, lo, hi);
+        mt = fmaxf(lo, hi);
+    }
 
     // lazy reference max: keep mc while the tile max stays within kLazyTau
     const float mtc = mt * c;
@@ -239,10 +271,11 @@ __device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char
         }
     }
     // fixed tree: each (kb, u) slot group chains its 4 pairs, then
-    // ((00 + 01) + (10 + 11)), then the partner lane's half: x + y == y + x,
-    // so both halves of a column get the same bits
+    // ((00 + 01) + (10 + 11)), then (low lane half + high lane half)
     const float ls_half = (part[0][0] + part[0][1]) + (part[1][0] + part[1][1]);
-    const float ls = ls_half + __shfl_xor(ls_half, 32);
+    float ls_lo, ls_hi;
+    halves(ls_half, ls_lo, ls_hi);
+    const float ls = ls_lo + ls_hi;
     l = __builtin_fmaf(l, a, ls);
 
     // o * 1 == o exactly, so skipping the rescale when no column of the wave
@@ -265,16 +298,28 @@ __device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char
             }
         }
     }
+    if (NDB == 4) {
+        // schedule: 4 fragments (8 reads) ahead, then 1 MFMA per 2 reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    }
     mc = mcn;
 }
 
-template <int NDB>
+// One whole tile; kMask selects the masked form (needed only on a tile that
+// holds keys beyond some column's position).
+template <int NDB, bool kMask>
 __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
-                                          int64_t key0, int64_t pos, bool mask, float c, float& mc, float& l,
+                                          int64_t key0, int64_t pos, float c, float& mc, float& l,
                                           f32x16 (&o)[NDB], int dblk0) {
     f32x16 s0, s1;
     qk_tile(qf, sK, lane, s0, s1);
-    softmax_pv_tile<NDB>(s0, s1, sV, lane, key0, pos, mask, c, mc, l, o, dblk0);
+    softmax_pv_tile<NDB, kMask>(s0, s1, sV, lane, key0, pos, c, mc, l, o, dblk0);
 }
 
 // Fold weights of one chunk into the running total (scalars of one column,
