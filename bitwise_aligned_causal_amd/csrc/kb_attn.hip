@@ -182,13 +182,28 @@ struct DecodeArgs {
 };
 
 constexpr int kDecodeWaves = 4;
+// Two stages (64 KiB of LDS) let two decode workgroups share a CU; measured
+// on B=16, L=8192 this streams faster than one workgroup with a deeper ring.
+constexpr int kDecodeStages = 2;
+
+// Wait until at most `ahead` tiles of this wave's decode loads are pending.
+__device__ __forceinline__ void wait_tiles_decode(int ahead) {
+    constexpr int per = kTileLoads / kDecodeWaves;
+    switch (ahead) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<per>(); break;
+        case 2: wait_vm<2 * per>(); break;
+        case 3: wait_vm<3 * per>(); break;
+        default: wait_vm<4 * per>(); break;
+    }
+}
 
 // Workgroup = 4 waves on one (batch, KV head, chunk).  The four query heads
 // sit in MFMA columns 0..3 (the other columns hold zeros).  Every wave computes
 // the scores of the tile; wave w accumulates the output rows d = 32w..32w+31.
 // The chunk's tiles stream through a 3-stage LDS ring two tiles ahead.
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * kTileBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int x = blockIdx.x;
@@ -208,10 +223,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     const int t0 = chunk * kTilesPerChunk;
     const int t1 = min(t0 + kTilesPerChunk, n_tiles);
 
-    stage_issue(kbase, vbase, (int64_t)t0 * kTile, a.kv_len, smem, smem + kKBytes, lane, w, kDecodeWaves);
-    if (t0 + 1 < t1)
-        stage_issue(kbase, vbase, (int64_t)(t0 + 1) * kTile, a.kv_len, smem + kTileBytes,
-                    smem + kTileBytes + kKBytes, lane, w, kDecodeWaves);
+    // ring of kDecodeStages tiles, loads kDecodeStages - 1 tiles ahead
+#pragma unroll
+    for (int i = 0; i < kDecodeStages - 1; ++i) {
+        if (t0 + i < t1) {
+            char* nb = smem + i * kTileBytes;
+            stage_issue(kbase, vbase, (int64_t)(t0 + i) * kTile, a.kv_len, nb, nb + kKBytes, lane, w, kDecodeWaves);
+        }
+    }
 
     bf16x8 qf[8];
     {
@@ -228,16 +247,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     f32x16 acc[1];
     acc[0] = zero16();
     for (int t = t0; t < t1; ++t) {
-        if (t + 1 < t1)
-            wait_vm<kTileLoads / kDecodeWaves>();
-        else
-            wait_vm<0>();
+        // tiles issued after tile t and still allowed in flight
+        const int ahead = min(t1 - 1, t + kDecodeStages - 2) - t;
+        wait_tiles_decode(ahead);
         __syncthreads();
-        if (t + 2 < t1) {
-            char* nb = smem + ((t + 2 - t0) % kStages) * kTileBytes;
-            stage_issue(kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w, kDecodeWaves);
+        if (t + kDecodeStages - 1 < t1) {
+            char* nb = smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * kTileBytes;
+            stage_issue(kbase, vbase, (int64_t)(t + kDecodeStages - 1) * kTile, a.kv_len, nb, nb + kKBytes, lane, w,
+                        kDecodeWaves);
         }
-        const char* buf = smem + ((t - t0) % kStages) * kTileBytes;
+        const char* buf = smem + ((t - t0) % kDecodeStages) * kTileBytes;
         // only the context's last tile can hold keys beyond kv_len - 1
         if (t < n_tiles - 1)
             tile_step<1, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, a.c, mc, l, acc, w);
