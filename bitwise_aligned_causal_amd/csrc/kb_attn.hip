@@ -54,8 +54,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nbg = a.batch * a.n_kv_heads;
     const int x = blockIdx.x;
-    const int bg = x % nbg;                            // same (b, g) -> same XCD when nbg % 8 == 0
-    const int pb = a.pb_first + a.n_pb - 1 - x / nbg;  // longest rows first
+    int bg, pbr;
+    if ((nbg & 7) == 0) {
+        // workgroups are dispatched to the 8 XCDs round-robin (x % 8); give XCD
+        // k the (b, g) pairs k, k + 8, ... one after another, each pair's
+        // position blocks longest first, so the blocks running together on an
+        // XCD stream the same K/V tiles through its L2
+        const int i = x >> 3;
+        bg = (i / a.n_pb) * 8 + (x & 7);
+        pbr = i % a.n_pb;
+    } else {
+        bg = x % nbg;
+        pbr = x / nbg;
+    }
+    const int pb = a.pb_first + a.n_pb - 1 - pbr;
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
     const int n_q_heads = kGroup * a.n_kv_heads;
     const int head = kGroup * g + (w & 3);
@@ -71,10 +83,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
     const uint16_t* vbase = a.v + kvoff;
     const int t_last = pb;
 
-    stage_issue(kbase, vbase, 0, a.kv_len, smem, smem + kKBytes, lane, w, kPrefillWaves);
+    StagePlan<kPrefillWaves> plan;
+    stage_plan(plan, lane, w);
+    stage_tile(plan, kbase, vbase, 0, a.kv_len, smem, smem + kKBytes, lane, w);
     if (t_last >= 1)
-        stage_issue(kbase, vbase, kTile, a.kv_len, smem + kTileBytes, smem + kTileBytes + kKBytes, lane, w,
-                    kPrefillWaves);
+        stage_tile(plan, kbase, vbase, kTile, a.kv_len, smem + kTileBytes, smem + kTileBytes + kKBytes, lane, w);
 
     bf16x8 qf[8];
     {
@@ -109,8 +122,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
         __syncthreads();
         if (t + 2 <= t_last) {
             char* nb = smem + ((t + 2) % kStages) * kTileBytes;
-            stage_issue(kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w,
-                        kPrefillWaves);
+            stage_tile(plan, kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w);
         }
     };
     auto close_chunk = [&]() {
@@ -224,11 +236,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     const int t1 = min(t0 + kTilesPerChunk, n_tiles);
 
     // ring of kDecodeStages tiles, loads kDecodeStages - 1 tiles ahead
+    StagePlan<kDecodeWaves> plan;
+    stage_plan(plan, lane, w);
 #pragma unroll
     for (int i = 0; i < kDecodeStages - 1; ++i) {
         if (t0 + i < t1) {
             char* nb = smem + i * kTileBytes;
-            stage_issue(kbase, vbase, (int64_t)(t0 + i) * kTile, a.kv_len, nb, nb + kKBytes, lane, w, kDecodeWaves);
+            stage_tile(plan, kbase, vbase, (int64_t)(t0 + i) * kTile, a.kv_len, nb, nb + kKBytes, lane, w);
         }
     }
 
@@ -253,8 +267,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         __syncthreads();
         if (t + kDecodeStages - 1 < t1) {
             char* nb = smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * kTileBytes;
-            stage_issue(kbase, vbase, (int64_t)(t + kDecodeStages - 1) * kTile, a.kv_len, nb, nb + kKBytes, lane, w,
-                        kDecodeWaves);
+            stage_tile(plan, kbase, vbase, (int64_t)(t + kDecodeStages - 1) * kTile, a.kv_len, nb, nb + kKBytes,
+                       lane, w);
         }
         const char* buf = smem + ((t - t0) % kDecodeStages) * kTileBytes;
         // only the context's last tile can hold keys beyond kv_len - 1

@@ -105,6 +105,72 @@ __device__ __forceinline__ void stage_issue(const uint16_t* kbase, const uint16_
     }
 }
 
+// Per-wave plan of the direct loads of a tile for a workgroup of NW waves:
+// wave w issues instructions i = w, w + NW, ...; the first half of them fill
+// K, the second half V.  off[k] is the byte offset, from the tile's first key
+// row, of the 16-byte chunk lane L fetches in its k-th instruction; it does
+// not depend on the tile, so it is computed once.
+template <int NW>
+struct StagePlan {
+    static constexpr int kN = kTileLoads / NW;
+    static_assert(kTileLoads % NW == 0 && NW <= 16, "each wave issues whole K and V halves");
+    uint32_t off[kN];
+};
+
+template <int NW>
+__device__ __forceinline__ void stage_plan(StagePlan<NW>& p, int lane, int wave) {
+#pragma unroll
+    for (int k = 0; k < StagePlan<NW>::kN; ++k) {
+        const int i = wave + k * NW;
+        const bool is_v = k >= StagePlan<NW>::kN / 2;
+        const int row = 4 * (i & 15) + (lane >> 4);
+        const int c = (lane & 15) ^ (is_v ? v_swz(row) : k_swz(row));
+        p.off[k] = (uint32_t)(row * 256 + c * 16);
+    }
+}
+
+__device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, const char* dst) {
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory");
+}
+
+// Issue this wave's loads of the tile starting at key0, which must lie wholly
+// below kv_len: a scalar tile base plus the planned per-lane offsets.
+template <int NW>
+__device__ __forceinline__ void stage_issue_full(const StagePlan<NW>& p, const uint16_t* kbase,
+                                                 const uint16_t* vbase, int64_t key0, char* sK, char* sV,
+                                                 int wave) {
+    const char* kt = reinterpret_cast<const char*>(kbase + key0 * kHeadDim);
+    const char* vt = reinterpret_cast<const char*>(vbase + key0 * kHeadDim);
+#pragma unroll
+    for (int k = 0; k < StagePlan<NW>::kN; ++k) {
+        const int i = wave + k * NW;
+        const bool is_v = k >= StagePlan<NW>::kN / 2;
+        lds_dma16(is_v ? vt : kt, p.off[k], (is_v ? sV : sK) + 1024 * (i & 15));
+    }
+}
+
+// Either form, chosen per tile (uniform branch).
+template <int NW>
+__device__ __forceinline__ void stage_tile(const StagePlan<NW>& p, const uint16_t* kbase, const uint16_t* vbase,
+                                           int64_t key0, int64_t kv_len, char* sK, char* sV, int lane,
+                                           int wave) {
+    if (key0 + kTile <= kv_len)
+        stage_issue_full<NW>(p, kbase, vbase, key0, sK, sV, wave);
+    else
+        stage_issue(kbase, vbase, key0, kv_len, sK, sV, lane, wave, NW);
+}
+
 // Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
