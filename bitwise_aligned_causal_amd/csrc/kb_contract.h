@@ -283,10 +283,13 @@ __device__ __forceinline__ void qk_tile(const bf16x8 (&qf)[8], const char* sK, i
 }
 
 // Mask, online-softmax update and P V of one tile whose scores are s0, s1.
-template <int NDB, bool kMask>
-__device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char* sV, int lane, int64_t key0,
-                                                int64_t pos, float c, float& mc, float& l, f32x16 (&o)[NDB],
-                                                int dblk0) {
+// Mask and online-softmax update of one tile whose scores are s0, s1:
+// updates (mc, l) and returns the O rescale factor a, whether any column of
+// the wave has a != 1, and the bf16 P^T operands pf[kb][u] of the tile's four
+// 16-key steps.
+template <bool kMask>
+__device__ __forceinline__ void sm_tile(f32x16 s0, f32x16 s1, int lane, int64_t key0, int64_t pos, float c,
+                                        float& mc, float& l, float& a, bool& any_grow, bf16x8 (&pf)[2][2]) {
     const int h = lane >> 5;
     if (kMask) {
         const float ninf = -__builtin_inff();
@@ -310,10 +313,10 @@ __device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char
     const float mtc = mt * c;
     const bool grow = (mtc - mc) > kLazyTau;
     const float mcn = grow ? mtc : mc;
-    const float a = grow ? exp2_hw(mc - mcn) : 1.0f;
+    a = grow ? exp2_hw(mc - mcn) : 1.0f;
+    any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
     const float nmc = -mcn;
 
-    bf16x8 pf[2][2];
     float part[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -337,22 +340,32 @@ __device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char
         }
     }
     // fixed tree: each (kb, u) slot group chains its 4 pairs, then
-    // ((00 + 01) + (10 + 11)), then (low lane half + high lane half)
+    // ((00 + 01) + (10 + 11)) per lane half, then (low half + high half)
     const float ls_half = (part[0][0] + part[0][1]) + (part[1][0] + part[1][1]);
     float ls_lo, ls_hi;
     halves(ls_half, ls_lo, ls_hi);
     const float ls = ls_lo + ls_hi;
     l = __builtin_fmaf(l, a, ls);
+    mc = mcn;
+}
 
-    // o * 1 == o exactly, so skipping the rescale when no column of the wave
-    // moved its reference max leaves every bit as it is
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+// o *= a.  o * 1 == o exactly, so skipping the multiply when no column of
+// the wave moved its reference max leaves every bit as it is.
+template <int NDB>
+__device__ __forceinline__ void rescale_o(f32x16 (&o)[NDB], float a, bool any_grow) {
+    if (any_grow) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) o[db][v] = o[db][v] * a;
         }
     }
+}
+
+// o += P V for one tile, key steps in order (kb, u) = (0,0), (0,1), (1,0), (1,1).
+template <int NDB>
+__device__ __forceinline__ void pv_tile(const bf16x8 (&pf)[2][2], const char* sV, int lane, f32x16 (&o)[NDB],
+                                        int dblk0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -374,18 +387,91 @@ __device__ __forceinline__ void softmax_pv_tile(f32x16 s0, f32x16 s1, const char
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
-    mc = mcn;
+}
+
+// P of one 16-key step (kb, u): 8 exps, 4 paired converts, and the step's
+// chain of 4 dot2 row-sum partials.
+__device__ __forceinline__ void p_step(const f32x16& s, int u, float c, float nmc, bf16x8& pf, float& part) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        f32x2 pp;
+        pp[0] = exp2_hw(__builtin_fmaf(s[8 * u + e], c, nmc));
+        pp[1] = exp2_hw(__builtin_fmaf(s[8 * u + e + 1], c, nmc));
+        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+        pf[e] = pb[0];
+        pf[e + 1] = pb[1];
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, acc, false);
+    }
+    part = acc;
+}
+
+// o += P V for one 16-key step (kb, u) over the wave's NDB d blocks.
+template <int NDB>
+__device__ __forceinline__ void pv_step(const bf16x8& pf, const char* sV, int kb, int u, int lane, f32x16 (&o)[NDB],
+                                        int dblk0) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const bf16x8 vf = vt_frag(sV, kb, u, dblk0 + db, lane);
+        o[db] = mfma(vf, pf, o[db]);
+    }
 }
 
 // One whole tile; kMask selects the masked form (needed only on a tile that
-// holds keys beyond some column's position).
+// holds keys beyond some column's position).  The arithmetic is that of
+// sm_tile + rescale_o + pv_tile; P is produced one 16-key step at a time so
+// that a step's P V products can run beside the next step's exponentials.
 template <int NDB, bool kMask>
 __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
                                           int64_t key0, int64_t pos, float c, float& mc, float& l,
                                           f32x16 (&o)[NDB], int dblk0) {
+    const int h = lane >> 5;
     f32x16 s0, s1;
     qk_tile(qf, sK, lane, s0, s1);
-    softmax_pv_tile<NDB, kMask>(s0, s1, sV, lane, key0, pos, c, mc, l, o, dblk0);
+    if (kMask) {
+        const float ninf = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
+            s0[v] = kk > pos ? ninf : s0[v];
+            s1[v] = kk + 32 > pos ? ninf : s1[v];
+        }
+    }
+    float mt = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mt = max3(mt, s0[v], s1[v]);
+    {
+        float lo, hi;
+        halves(mt, lo, hi);
+        mt = fmaxf(lo, hi);
+    }
+    const float mtc = mt * c;
+    const bool grow = (mtc - mc) > kLazyTau;
+    const float mcn = grow ? mtc : mc;
+    const float a = grow ? exp2_hw(mc - mcn) : 1.0f;
+    const bool any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
+    const float nmc = -mcn;
+
+    bf16x8 pf[2][2];
+    float part[2][2];
+    p_step(s0, 0, c, nmc, pf[0][0], part[0][0]);
+    rescale_o<NDB>(o, a, any_grow);
+    pv_step<NDB>(pf[0][0], sV, 0, 0, lane, o, dblk0);
+    p_step(s0, 1, c, nmc, pf[0][1], part[0][1]);
+    pv_step<NDB>(pf[0][1], sV, 0, 1, lane, o, dblk0);
+    p_step(s1, 0, c, nmc, pf[1][0], part[1][0]);
+    pv_step<NDB>(pf[1][0], sV, 1, 0, lane, o, dblk0);
+    p_step(s1, 1, c, nmc, pf[1][1], part[1][1]);
+    pv_step<NDB>(pf[1][1], sV, 1, 1, lane, o, dblk0);
+
+    // fixed tree: ((00 + 01) + (10 + 11)) per lane half, then (low + high)
+    const float ls_half = (part[0][0] + part[0][1]) + (part[1][0] + part[1][1]);
+    float ls_lo, ls_hi;
+    halves(ls_half, ls_lo, ls_hi);
+    const float ls = ls_lo + ls_hi;
+    l = __builtin_fmaf(l, a, ls);
+    mc = mcn;
 }
 
 // Fold weights of one chunk into the running total (scalars of one column,
