@@ -6,9 +6,11 @@ The GPU runs (each command runs committed files only):
   rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
   rocprofv3 --pmc FETCH_SIZE -d <copy_fetch> -o run --output-format csv -- python3 bench.py --copy-probe
   rocprofv3 --pmc WRITE_SIZE -d <copy_write> -o run --output-format csv -- python3 bench.py --copy-probe
+  rocprofv3 --pmc <8 SQ counters> -d <sqN> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
+      (two passes, SQ_PASSES below)
 Then, on any host:
   python bench_profile.py --stats <stats> --fetch <fetch> --write <write> \
-      --copy-fetch <copy_fetch> --copy-write <copy_write> --out profiles
+      --copy-fetch <copy_fetch> --copy-write <copy_write> [--sq <sq1> <sq2>] --out profiles
 
 FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  Each is scaled by the
 factor that makes the plain 1 GiB copy read and write exactly 1 GiB.
@@ -25,6 +27,12 @@ import statistics
 import bench
 
 COPY_BYTES = 1 << 30
+SQ_PASSES = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+    "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS",
+    "SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU "
+    "SQ_LDS_ADDR_CONFLICT SQ_INSTS_VALU_MFMA_MOPS_BF16",
+)
 KERNELS = {
     "prefill_kernel<false>": ("prefill_kernel_b16_s16384", "full causal prefill B=16 S=16384 (one launch per step)"),
     "prefill_kernel<true>": ("prefill_kernel_partitioned_b16_16x1024",
@@ -62,10 +70,45 @@ def copy_factor(d: str) -> float:
     return COPY_BYTES / 1024.0 / statistics.mean(vals)
 
 
+def prefill_wave_tiles() -> int:
+    """64-key tiles visited per wave, summed over the full-prefill launch:
+    a workgroup covers 4 heads x 64 positions with 8 waves, and position
+    block pb visits pb + 1 tiles."""
+    blocks = bench.S // 64
+    return bench.B * (bench.HQ // 4) * (blocks * (blocks + 1) // 2) * 8
+
+
+def sq_summary(dirs, out: str, src_hash: str) -> None:
+    vals = {}
+    for d in dirs:
+        for name, rows in per_counter(d).items():
+            vals.update(rows)
+    tiles = prefill_wave_tiles()
+    lines = [f"# prefill_kernel<false> SQ counters, B={bench.B} S={bench.S} ({tiles / 8:.3g} workgroup-tiles x 8 waves)",
+             f"kernel source hash: {src_hash}", "",
+             "commands (one pass each, counters split to stay within the SQ block limit):"]
+    lines += [f"  rocprofv3 --pmc {p} -d <dir> -o run --output-format csv -- "
+              "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline" for p in SQ_PASSES]
+    lines += ["", "values for the full-prefill dispatch (SQ_WAVE_CYCLES and SQ_ACTIVE_* are in 4-cycle units):"]
+    lines += [f"  {k:<32} {v:>12.4g}   per wave per 64-key tile {v / tiles:>9.2f}" for k, v in sorted(vals.items())]
+    with open(os.path.join(out, "prefill_kernel_b16_s16384_sq_counters.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def per_counter(d: str):
+    """{kernel: {counter: value}} for the full-prefill dispatch of one pass."""
+    out = {}
+    for r in csv.DictReader(open(find_csv(d, "counter_collection.csv"))):
+        if short(r["Kernel_Name"]) == "prefill_kernel<false>":
+            out.setdefault("prefill_kernel<false>", {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     for a in ("stats", "fetch", "write", "copy_fetch", "copy_write", "out"):
         ap.add_argument("--" + a.replace("_", "-"), required=True)
+    ap.add_argument("--sq", nargs="*", default=[], help="directories of the SQ counter passes")
     args = ap.parse_args()
     f_fetch, f_write = copy_factor(args.copy_fetch), copy_factor(args.copy_write)
     stats = {}
@@ -120,6 +163,8 @@ def main():
         with open(os.path.join(args.out, fname + "_traffic.json"), "w") as fh:
             json.dump(rec, fh, indent=1)
         print(f"{k}: avg {rec['avg_duration_us']:.1f} us, HBM {hbm:.3e} B/launch")
+    if args.sq:
+        sq_summary(args.sq, args.out, src_hash)
 
 
 if __name__ == "__main__":
