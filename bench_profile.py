@@ -91,6 +91,11 @@ def sq_summary(dirs, out: str, src_hash: str) -> None:
               "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline" for p in SQ_PASSES]
     lines += ["", "values for the full-prefill dispatch (SQ_WAVE_CYCLES and SQ_ACTIVE_* are in 4-cycle units):"]
     lines += [f"  {k:<32} {v:>12.4g}   per wave per 64-key tile {v / tiles:>9.2f}" for k, v in sorted(vals.items())]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "SQ_BUSY_CU_CYCLES" in vals:
+        # MFMA busy cycles are summed over SIMDs, CU busy cycles over CUs (4 SIMDs each)
+        util = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * vals["SQ_BUSY_CU_CYCLES"])
+        lines += ["", f"MFMA utilisation: SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES) = {util:.3f} of the "
+                      "SIMD cycles while the CUs are busy (at the clock the chip runs under this load)"]
     with open(os.path.join(out, "prefill_kernel_b16_s16384_sq_counters.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
