@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -50,10 +51,15 @@ def prefill_flops(batch: int, n_rows_first_pos: int, n_rows: int) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so that
+    a counter summary stays valid across edits that change no code."""
     h = hashlib.sha256()
     for name in ("kb_attn.hip", "kb_contract.h"):
-        with open(os.path.join(ROOT, "bitwise_aligned_causal_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bitwise_aligned_causal_amd", "csrc", name)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

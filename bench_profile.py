@@ -85,7 +85,7 @@ def sq_summary(dirs, out: str, src_hash: str) -> None:
             vals.update(rows)
     tiles = prefill_wave_tiles()
     lines = [f"# prefill_kernel<false> SQ counters, B={bench.B} S={bench.S} ({tiles / 8:.3g} workgroup-tiles x 8 waves)",
-             f"kernel source hash: {src_hash}", "",
+             f"kernel source hash (code without comments): {src_hash}", "",
              "commands (one pass each, counters split to stay within the SQ block limit):"]
     lines += [f"  rocprofv3 --pmc {p} -d <dir> -o run --output-format csv -- "
               "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline" for p in SQ_PASSES]
@@ -135,7 +135,7 @@ def main():
         hbm = (fetch_kib * f_fetch + write_kib * f_write) * 1024.0
         lines = [
             f"# {k}: {what}",
-            f"kernel source hash: {src_hash}",
+            f"kernel source hash (code without comments): {src_hash}",
             "",
             "commands:",
             "  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- "

@@ -213,7 +213,7 @@ __device__ __forceinline__ void wait_tiles_decode(int ahead) {
 // Workgroup = 4 waves on one (batch, KV head, chunk).  The four query heads
 // sit in MFMA columns 0..3 (the other columns hold zeros).  Every wave computes
 // the scores of the tile; wave w accumulates the output rows d = 32w..32w+31.
-// The chunk's tiles stream through a 3-stage LDS ring two tiles ahead.
+// The chunk's tiles stream through a kDecodeStages-deep LDS ring.
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * kTileBytes];
     const int tid = threadIdx.x, lane = tid & 63;

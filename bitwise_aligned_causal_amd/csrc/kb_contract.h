@@ -227,7 +227,11 @@ __device__ __forceinline__ void halves(float x, float& lo, float& hi) {
 }
 
 // max of three floats (exact; written as one instruction so that no
-// canonicalising moves are inserted for MFMA results)
+// canonicalising moves are inserted for MFMA results).  The compiler does not
+// see inside the asm, so it would not wait for an MFMA result read here: the
+// first read of every score block is ordinary code (the fmaxf that starts the
+// max tree), which makes the compiler wait for the products; max3 then reads
+// registers that are already complete.
 __device__ __forceinline__ float max3(float a, float b, float c) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
