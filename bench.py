@@ -206,6 +206,28 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
+
+    # decode sweep: batch 1/4/8/16 x context 128/1K/4K/8K over the resident
+    # cache (capacity 16384, first kv_len keys), cold, one query token per head
+    sweep = []
+    for bs in (1, 4, 8, 16):
+        for ctx in (128, 1024, 4096, 8192):
+            qs = qd[:bs, :, ctx - 1:ctx].contiguous()
+            os_ = torch.empty_like(qs)
+            wss = torch.empty(max(1, kb.decode_workspace_bytes(bs, ctx, HQ, D)), dtype=torch.uint8, device=dev)
+            kv_b, vv_b = kd[:bs], vd[:bs]
+            reps = []
+            for i in range(11):
+                flush.sum()
+                e0.record(stream)
+                kb.decode(qs, kv_b, vv_b, kv_len=ctx, out=os_, workspace=wss)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                reps.append(e0.elapsed_time(e1))
+            us = float(np.median(reps[1:])) * 1e3
+            nbytes = 4096 * bs * ctx + 16384 * bs
+            sweep.append({"batch": bs, "kv_len": ctx, "us_cold": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+                          "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / PEAK_HBM, 4)})
     del flush
 
     pre_ms = float(np.mean(times["pre"]))
@@ -243,6 +265,7 @@ def main() -> int:
                    "gbs_in_step": round(dec_bytes / dec_ms / 1e6, 1),
                    "ms_cold": round(cold_ms, 4), "gbs_cold": round(dec_bytes / cold_ms / 1e6, 1),
                    "frac_of_peak_cold": round(dec_bytes / (cold_ms * 1e-3) / PEAK_HBM, 4)},
+        "decode_sweep": sweep,
         "bitwise_mismatch": {"partitioned_vs_prefill": mism, "decode_vs_prefill": mism_dec},
         "contract": kb.contract(),
         "kernel_source_hash": kernel_source_hash(),

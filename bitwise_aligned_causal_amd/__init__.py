@@ -11,7 +11,9 @@ Entry points (KernelBraid / AReaL-TIK README, "Usage" and "Method"):
   partitioned(q, k_cache, v_cache, kv_len)  a chunk of rows against cached KV
   decode(q, k_cache, v_cache, kv_len)       one query token
   unified_prefill / unified_decode          the README's call shapes
-All three give bitwise-identical rows for the same inputs and context.
+  prefill_varlen / partitioned_varlen / decode_varlen
+                                            ragged batches, packed [heads, rows, 128]
+All of them give bitwise-identical rows for the same inputs and context.
 """
 from __future__ import annotations
 
@@ -53,6 +55,16 @@ def lib() -> ctypes.CDLL:
         L.kb_attn_decode.restype = ctypes.c_int
         L.kb_attn_decode_workspace_bytes.argtypes = [i64, i64, i32, i32]
         L.kb_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        p64 = ctypes.POINTER(i64)
+        L.kb_attn_prefill_varlen.argtypes = [vp, vp, vp, vp, p64, i64, i32, i32, i32, f32, vp]
+        L.kb_attn_prefill_varlen.restype = ctypes.c_int
+        L.kb_attn_partitioned_varlen.argtypes = [vp, vp, vp, vp, p64, p64, p64, i64, i32, i32, i32, f32, vp]
+        L.kb_attn_partitioned_varlen.restype = ctypes.c_int
+        L.kb_attn_decode_varlen.argtypes = [vp, vp, vp, vp, p64, p64, i64, i32, i32, i32, f32, vp, ctypes.c_size_t,
+                                            vp]
+        L.kb_attn_decode_varlen.restype = ctypes.c_int
+        L.kb_attn_decode_varlen_workspace_bytes.argtypes = [p64, i64, i32, i32]
+        L.kb_attn_decode_varlen_workspace_bytes.restype = ctypes.c_size_t
         L.kb_attn_strerror.argtypes = [ctypes.c_int]
         L.kb_attn_strerror.restype = ctypes.c_char_p
         L.kb_attn_contract.argtypes = [ctypes.POINTER(i32)] * 3
@@ -77,6 +89,17 @@ def decode_workspace_bytes(batch: int, kv_len: int, n_q_heads: int = 32, head_di
     return int(lib().kb_attn_decode_workspace_bytes(batch, kv_len, n_q_heads, head_dim))
 
 
+def _host_i64(values):
+    """A ctypes int64 array holding `values` (host memory, kept alive by the caller)."""
+    vals = [int(x) for x in values]
+    return (ctypes.c_int64 * max(1, len(vals)))(*vals)
+
+
+def decode_varlen_workspace_bytes(kv_lens, n_q_heads: int = 32, head_dim: int = HEAD_DIM) -> int:
+    arr = _host_i64(kv_lens)
+    return int(lib().kb_attn_decode_varlen_workspace_bytes(arr, len(kv_lens), n_q_heads, head_dim))
+
+
 def _torch():
     import torch
     return torch
@@ -87,7 +110,7 @@ def _check_tensor(name, x, ndim=4):
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != ndim or not x.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous 4-D bfloat16 tensor on the GPU "
+        raise ValueError(f"{name} must be a contiguous {ndim}-D bfloat16 tensor on the GPU "
                          f"(got {x.dtype}, {x.device}, shape {tuple(x.shape)})")
 
 
@@ -151,6 +174,77 @@ def decode(q, k_cache, v_cache, kv_len: int | None = None, scale: float | None =
     check(lib().kb_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B, kv_len,
                                k_cache.shape[2], Hq, k_cache.shape[1], D, _scale(scale, D), ws_ptr, ws_bytes,
                                _stream(q)))
+    return out
+
+
+def _check_packed(name, x):
+    _check_tensor(name, x, ndim=3)
+    if x.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be [heads, rows, {HEAD_DIM}]")
+
+
+def prefill_varlen(q, k, v, cu_seqlens, scale: float | None = None, out=None):
+    """Ragged causal prefill.  q [Hq, T, 128], k/v [Hkv, T, 128] packed
+    head-major; sequence i owns rows cu_seqlens[i] .. cu_seqlens[i+1] - 1
+    (host list of batch + 1 offsets, T = cu_seqlens[-1])."""
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _check_packed(n, x)
+    if k.shape != v.shape or k.shape[1] != q.shape[1]:
+        raise ValueError("k/v must be [Hkv, T, 128] with the rows of q")
+    cu = _host_i64(cu_seqlens)
+    if int(cu_seqlens[-1]) != q.shape[1]:
+        raise ValueError("cu_seqlens[-1] must equal the packed row count")
+    out = _torch().empty_like(q) if out is None else out
+    _check_packed("out", out)
+    check(lib().kb_attn_prefill_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu,
+                                       len(cu_seqlens) - 1, q.shape[0], k.shape[0], HEAD_DIM,
+                                       _scale(scale, HEAD_DIM), _stream(q)))
+    return out
+
+
+def partitioned_varlen(q, k_cache, v_cache, cu_q, cu_cache, kv_lens, scale: float | None = None, out=None):
+    """Ragged partitioned forward.  q [Hq, cu_q[-1], 128]; caches [Hkv,
+    cu_cache[-1], 128]; sequence i has cu_q[i+1] - cu_q[i] query rows ending at
+    position kv_lens[i] - 1, against the first kv_lens[i] rows of its cache
+    range cu_cache[i] .. cu_cache[i+1] - 1 (host lists)."""
+    for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_packed(n, x)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("cache shape mismatch")
+    if int(cu_q[-1]) != q.shape[1] or int(cu_cache[-1]) != k_cache.shape[1]:
+        raise ValueError("offsets do not match the packed row counts")
+    batch = len(cu_q) - 1
+    if len(cu_cache) != batch + 1 or len(kv_lens) != batch:
+        raise ValueError("cu_q, cu_cache and kv_lens describe different batch sizes")
+    a_q, a_c, a_l = _host_i64(cu_q), _host_i64(cu_cache), _host_i64(kv_lens)
+    out = _torch().empty_like(q) if out is None else out
+    _check_packed("out", out)
+    check(lib().kb_attn_partitioned_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                           a_q, a_c, a_l, batch, q.shape[0], k_cache.shape[0], HEAD_DIM,
+                                           _scale(scale, HEAD_DIM), _stream(q)))
+    return out
+
+
+def decode_varlen(q, k_cache, v_cache, cu_cache, kv_lens, scale: float | None = None, out=None, workspace=None):
+    """Ragged one-token decode.  q [Hq, batch, 128] (row i is sequence i's
+    token at position kv_lens[i] - 1); caches [Hkv, cu_cache[-1], 128]."""
+    torch = _torch()
+    for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_packed(n, x)
+    batch = q.shape[1]
+    if len(cu_cache) != batch + 1 or len(kv_lens) != batch or int(cu_cache[-1]) != k_cache.shape[1]:
+        raise ValueError("cu_cache / kv_lens do not match q and the caches")
+    need = decode_varlen_workspace_bytes(kv_lens, q.shape[0])
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a_c, a_l = _host_i64(cu_cache), _host_i64(kv_lens)
+    out = torch.empty_like(q) if out is None else out
+    _check_packed("out", out)
+    check(lib().kb_attn_decode_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), a_c,
+                                      a_l, batch, q.shape[0], k_cache.shape[0], HEAD_DIM, _scale(scale, HEAD_DIM),
+                                      ws_ptr, ws_bytes, _stream(q)))
     return out
 
 

@@ -17,7 +17,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
+#include <vector>
 
 #include "../../include/kb_attn.h"
 #include "kb_contract.h"
@@ -40,6 +42,17 @@ struct PrefillArgs {
 constexpr int kPrefillWaves = 8;
 constexpr int kStages = 3;
 
+// Everything a prefill workgroup needs once its work item is known.
+struct PrefillWork {
+    const uint16_t* q0;  // row 0 of this (sequence, KV head group): query head 4g + i at q0 + i * q_hstride rows
+    uint16_t* o0;        // same for the output
+    int64_t q_hstride;   // rows between consecutive query heads
+    const uint16_t* kbase;  // key 0 of this (sequence, KV head)
+    const uint16_t* vbase;
+    int64_t q_len, kv_len;
+    int pb;  // 64-position block
+};
+
 // Workgroup = 8 waves = the 4 query heads of one KV head x 2 halves of the 64
 // absolute positions [64 pb, 64 pb + 64).  Every row of the block has its last
 // visible key in tile pb, so all rows visit exactly the tiles 0..pb and never
@@ -48,50 +61,32 @@ constexpr int kStages = 3;
 // kPartitioned = false is the full-sequence case (q_len == kv_len, row r at
 // position r); both instantiations run the same per-row arithmetic.
 template <bool kPartitioned>
-__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
+__device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nbg = a.batch * a.n_kv_heads;
-    const int x = blockIdx.x;
-    int bg, pbr;
-    if ((nbg & 7) == 0) {
-        // workgroups are dispatched to the 8 XCDs round-robin (x % 8); give XCD
-        // k the (b, g) pairs k, k + 8, ... one after another, each pair's
-        // position blocks longest first, so the blocks running together on an
-        // XCD stream the same K/V tiles through its L2
-        const int i = x >> 3;
-        bg = (i / a.n_pb) * 8 + (x & 7);
-        pbr = i % a.n_pb;
-    } else {
-        bg = x % nbg;
-        pbr = x / nbg;
-    }
-    const int pb = a.pb_first + a.n_pb - 1 - pbr;
-    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
-    const int n_q_heads = kGroup * a.n_kv_heads;
-    const int head = kGroup * g + (w & 3);
+    const int pb = wk.pb;
     const int j = lane & 31, h = lane >> 5;
 
-    const int64_t off = kPartitioned ? a.kv_len - a.q_len : 0;
+    const int64_t off = kPartitioned ? wk.kv_len - wk.q_len : 0;
     const int64_t pos = (int64_t)pb * 64 + 32 * (w >> 2) + j;
     const int64_t r = pos - off;
-    const bool active = r >= 0 && r < a.q_len;
+    const bool active = r >= 0 && r < wk.q_len;
 
-    const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
-    const uint16_t* kbase = a.k + kvoff;
-    const uint16_t* vbase = a.v + kvoff;
+    const uint16_t* kbase = wk.kbase;
+    const uint16_t* vbase = wk.vbase;
+    const int64_t kv_len = wk.kv_len;
     const int t_last = pb;
 
     StagePlan<kPrefillWaves> plan;
     stage_plan(plan, lane, w);
-    stage_tile(plan, kbase, vbase, 0, a.kv_len, smem, smem + kKBytes, lane, w);
+    stage_tile(plan, kbase, vbase, 0, kv_len, smem, smem + kKBytes, lane, w);
     if (t_last >= 1)
-        stage_tile(plan, kbase, vbase, kTile, a.kv_len, smem + kTileBytes, smem + kTileBytes + kKBytes, lane, w);
+        stage_tile(plan, kbase, vbase, kTile, kv_len, smem + kTileBytes, smem + kTileBytes + kKBytes, lane, w);
 
+    const int64_t qrow0 = (int64_t)(w & 3) * wk.q_hstride;  // this wave's query head
     bf16x8 qf[8];
     {
-        const uint16_t* qrow = a.q + (((int64_t)b * n_q_heads + head) * a.q_len + (active ? r : 0)) * kHeadDim;
+        const uint16_t* qrow = wk.q0 + (qrow0 + (active ? r : 0)) * kHeadDim;
         const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
@@ -122,7 +117,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
         __syncthreads();
         if (t + 2 <= t_last) {
             char* nb = smem + ((t + 2) % kStages) * kTileBytes;
-            stage_tile(plan, kbase, vbase, (int64_t)(t + 2) * kTile, a.kv_len, nb, nb + kKBytes, lane, w);
+            stage_tile(plan, kbase, vbase, (int64_t)(t + 2) * kTile, kv_len, nb, nb + kKBytes, lane, w);
         }
     };
     auto close_chunk = [&]() {
@@ -153,19 +148,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
     for (int t = 0; t < t_last; ++t) {
         publish(t);
         const char* buf = smem + (t % kStages) * kTileBytes;
-        tile_step<4, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, a.c, mc, l, acc, 0);
+        tile_step<4, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, 0);
         if ((t % kTilesPerChunk) == kTilesPerChunk - 1) close_chunk();
     }
     // the diagonal tile t_last holds keys beyond some rows' positions
     {
         publish(t_last);
         const char* buf = smem + (t_last % kStages) * kTileBytes;
-        tile_step<4, true>(qf, buf, buf + kKBytes, lane, (int64_t)t_last * kTile, pos, a.c, mc, l, acc, 0);
+        tile_step<4, true>(qf, buf, buf + kKBytes, lane, (int64_t)t_last * kTile, pos, c, mc, l, acc, 0);
         close_chunk();
     }
 
     if (active) {
-        uint16_t* orow = a.o + (((int64_t)b * n_q_heads + head) * a.q_len + r) * kHeadDim;
+        uint16_t* orow = wk.o0 + (qrow0 + r) * kHeadDim;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -179,6 +174,86 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
             }
         }
     }
+}
+
+// Dense batch: q, o [batch, Hq, q_len, 128]; k, v [batch, Hkv, cap, 128].
+template <bool kPartitioned>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
+    const int nbg = a.batch * a.n_kv_heads;
+    const int x = blockIdx.x;
+    int bg, pbr;
+    if ((nbg & 7) == 0) {
+        // workgroups are dispatched to the 8 XCDs round-robin (x % 8); give XCD
+        // k the (b, g) pairs k, k + 8, ... one after another, each pair's
+        // position blocks longest first, so the blocks running together on an
+        // XCD stream the same K/V tiles through its L2
+        const int i = x >> 3;
+        bg = (i / a.n_pb) * 8 + (x & 7);
+        pbr = i % a.n_pb;
+    } else {
+        bg = x % nbg;
+        pbr = x / nbg;
+    }
+    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
+    const int n_q_heads = kGroup * a.n_kv_heads;
+    PrefillWork wk;
+    wk.q0 = a.q + ((int64_t)b * n_q_heads + kGroup * g) * a.q_len * kHeadDim;
+    wk.o0 = a.o + ((int64_t)b * n_q_heads + kGroup * g) * a.q_len * kHeadDim;
+    wk.q_hstride = a.q_len;
+    const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
+    wk.kbase = a.k + kvoff;
+    wk.vbase = a.v + kvoff;
+    wk.q_len = a.q_len;
+    wk.kv_len = a.kv_len;
+    wk.pb = a.pb_first + a.n_pb - 1 - pbr;
+    prefill_body<kPartitioned>(wk, a.c, smem);
+}
+
+// Ragged batch: the sequences of one launch (at most kMaxVarlenSeqs), packed
+// head-major: q, o [Hq, q_rows, 128]; k, v [Hkv, kv_rows, 128].  Sequence s
+// holds query rows q_row0[s] .. + q_len[s] - 1 and keys kv_row0[s] .. +
+// kv_len[s] - 1; its row r sits at position kv_len[s] - q_len[s] + r.
+constexpr int kMaxVarlenSeqs = 64;
+struct VarlenTable {
+    int64_t q_row0[kMaxVarlenSeqs];
+    int64_t kv_row0[kMaxVarlenSeqs];
+    int32_t q_len[kMaxVarlenSeqs];
+    int32_t kv_len[kMaxVarlenSeqs];
+    int32_t unit0[kMaxVarlenSeqs + 1];  // first work unit of each sequence (prefix sum)
+    int32_t n_seqs;
+};
+
+struct VarlenArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    int64_t q_rows, kv_rows;  // rows per head of the packed tensors
+    int32_t n_kv_heads;
+    float c;
+};
+
+// Work units of a sequence: (64-position block, KV head), longest blocks
+// first.  All rows use the partitioned form (q_len == kv_len gives position r).
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_varlen_kernel(VarlenArgs a, VarlenTable t) {
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
+    const int x = blockIdx.x;
+    int s = 0;
+    while (s + 1 < t.n_seqs && t.unit0[s + 1] <= x) ++s;
+    const int u = x - t.unit0[s];
+    const int g = u % a.n_kv_heads, pbr = u / a.n_kv_heads;
+    const int64_t q_len = t.q_len[s], kv_len = t.kv_len[s];
+    PrefillWork wk;
+    wk.q0 = a.q + ((int64_t)kGroup * g * a.q_rows + t.q_row0[s]) * kHeadDim;
+    wk.o0 = a.o + ((int64_t)kGroup * g * a.q_rows + t.q_row0[s]) * kHeadDim;
+    wk.q_hstride = a.q_rows;
+    wk.kbase = a.k + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
+    wk.vbase = a.v + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
+    wk.q_len = q_len;
+    wk.kv_len = kv_len;
+    wk.pb = (int)((kv_len - 1) / 64) - pbr;
+    prefill_body<true>(wk, a.c, smem);
 }
 
 struct DecodeArgs {
@@ -210,28 +285,35 @@ __device__ __forceinline__ void wait_tiles_decode(int ahead) {
     }
 }
 
-// Workgroup = 4 waves on one (batch, KV head, chunk).  The four query heads
+// Everything a decode workgroup needs once its work item is known.
+struct DecodeWork {
+    const uint16_t* q;  // query head 4g + i at row q_row0 + i * q_hstride
+    uint16_t* o;        // output rows, same indexing
+    int64_t q_row0, q_hstride;
+    const uint16_t* kbase;  // key 0 of this (sequence, KV head)
+    const uint16_t* vbase;
+    int64_t kv_len;
+    int chunk, n_chunks;
+    int64_t ws_row0;  // partial of query head 4g + i, this chunk: ws row ws_row0 + i * n_chunks + chunk
+};
+
+// Workgroup = 4 waves on one (sequence, KV head, chunk).  The four query heads
 // sit in MFMA columns 0..3 (the other columns hold zeros).  Every wave computes
 // the scores of the tile; wave w accumulates the output rows d = 32w..32w+31.
 // The chunk's tiles stream through a kDecodeStages-deep LDS ring.
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * kTileBytes];
+__device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, float* ws_ml, float c, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int x = blockIdx.x;
-    const int chunk = x % a.n_chunks;
-    const int bg = x / a.n_chunks;
-    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
-    const int n_q_heads = kGroup * a.n_kv_heads;
+    const int chunk = wk.chunk;
     const int j = lane & 31, h = lane >> 5;
     const bool active = j < kGroup;
-    const int head = kGroup * g + (active ? j : 0);
-    const int64_t pos = a.kv_len - 1;
+    const int hi = active ? j : 0;  // query head 4g + hi
+    const int64_t kv_len = wk.kv_len;
+    const int64_t pos = kv_len - 1;
 
-    const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
-    const uint16_t* kbase = a.k + kvoff;
-    const uint16_t* vbase = a.v + kvoff;
-    const int n_tiles = (int)((a.kv_len + kTile - 1) / kTile);
+    const uint16_t* kbase = wk.kbase;
+    const uint16_t* vbase = wk.vbase;
+    const int n_tiles = (int)((kv_len + kTile - 1) / kTile);
     const int t0 = chunk * kTilesPerChunk;
     const int t1 = min(t0 + kTilesPerChunk, n_tiles);
 
@@ -242,13 +324,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     for (int i = 0; i < kDecodeStages - 1; ++i) {
         if (t0 + i < t1) {
             char* nb = smem + i * kTileBytes;
-            stage_tile(plan, kbase, vbase, (int64_t)(t0 + i) * kTile, a.kv_len, nb, nb + kKBytes, lane, w);
+            stage_tile(plan, kbase, vbase, (int64_t)(t0 + i) * kTile, kv_len, nb, nb + kKBytes, lane, w);
         }
     }
 
+    const int64_t qrow_idx = wk.q_row0 + (int64_t)hi * wk.q_hstride;
     bf16x8 qf[8];
     {
-        const uint16_t* qrow = a.q + ((int64_t)b * n_q_heads + head) * kHeadDim;
+        const uint16_t* qrow = wk.q + qrow_idx * kHeadDim;
         const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
@@ -267,22 +350,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         __syncthreads();
         if (t + kDecodeStages - 1 < t1) {
             char* nb = smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * kTileBytes;
-            stage_tile(plan, kbase, vbase, (int64_t)(t + kDecodeStages - 1) * kTile, a.kv_len, nb, nb + kKBytes,
+            stage_tile(plan, kbase, vbase, (int64_t)(t + kDecodeStages - 1) * kTile, kv_len, nb, nb + kKBytes,
                        lane, w);
         }
         const char* buf = smem + ((t - t0) % kDecodeStages) * kTileBytes;
         // only the context's last tile can hold keys beyond kv_len - 1
         if (t < n_tiles - 1)
-            tile_step<1, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, a.c, mc, l, acc, w);
+            tile_step<1, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, w);
         else
-            tile_step<1, true>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, a.c, mc, l, acc, w);
+            tile_step<1, true>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, w);
     }
 
     if (!active) return;
-    const int64_t row = (int64_t)b * n_q_heads + head;
-    if (a.n_chunks == 1) {
+    if (wk.n_chunks == 1) {
         // a single chunk is copied into the total: out = o / l
-        uint16_t* orow = a.o + row * kHeadDim;
+        uint16_t* orow = wk.o + qrow_idx * kHeadDim;
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
             const uint32_t e0 = finalize(acc[0][4 * b4 + 0], l), e1 = finalize(acc[0][4 * b4 + 1], l);
@@ -294,8 +376,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         }
         return;
     }
-    const int64_t prow = row * a.n_chunks + chunk;
-    float* po = a.ws_o + prow * kHeadDim;
+    const int64_t prow = wk.ws_row0 + (int64_t)hi * wk.n_chunks + chunk;
+    float* po = ws_o + prow * kHeadDim;
 #pragma unroll
     for (int b4 = 0; b4 < 4; ++b4) {
         float4 f;
@@ -306,9 +388,32 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         *reinterpret_cast<float4*>(po + 32 * w + 8 * b4 + 4 * h) = f;
     }
     if (w == 0 && h == 0) {
-        a.ws_ml[prow * 2 + 0] = mc;
-        a.ws_ml[prow * 2 + 1] = l;
+        ws_ml[prow * 2 + 0] = mc;
+        ws_ml[prow * 2 + 1] = l;
     }
+}
+
+// Dense batch: q, o [batch, Hq, 1, 128]; caches [batch, Hkv, cap, 128].
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * kTileBytes];
+    const int x = blockIdx.x;
+    const int chunk = x % a.n_chunks;
+    const int bg = x / a.n_chunks;
+    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
+    const int n_q_heads = kGroup * a.n_kv_heads;
+    DecodeWork wk;
+    wk.q = a.q;
+    wk.o = a.o;
+    wk.q_row0 = (int64_t)b * n_q_heads + kGroup * g;
+    wk.q_hstride = 1;
+    const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
+    wk.kbase = a.k + kvoff;
+    wk.vbase = a.v + kvoff;
+    wk.kv_len = a.kv_len;
+    wk.chunk = chunk;
+    wk.n_chunks = a.n_chunks;
+    wk.ws_row0 = wk.q_row0 * a.n_chunks;
+    decode_body(wk, a.ws_o, a.ws_ml, a.c, smem);
 }
 
 struct CombineArgs {
@@ -319,26 +424,92 @@ struct CombineArgs {
     float c;
 };
 
-// One workgroup per (batch, query head), one thread per output element d:
-// copy chunk 0, fold chunks 1.. in order, finalize.
-__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-    const int64_t row = blockIdx.x;
+// Fold the chunk partials of one output row in chunk order and finalize;
+// thread d owns output element d.
+__device__ __forceinline__ void combine_row(const float* ws_o, const float* ws_ml, int64_t base, int n_chunks,
+                                            uint16_t* orow) {
     const int d = threadIdx.x;
-    const int64_t base = row * a.n_chunks;
-    float Mc = a.ws_ml[base * 2 + 0];
-    float L = a.ws_ml[base * 2 + 1];
-    float O = a.ws_o[base * kHeadDim + d];
-    for (int k = 1; k < a.n_chunks; ++k) {
-        const float mc = a.ws_ml[(base + k) * 2 + 0];
-        const float l = a.ws_ml[(base + k) * 2 + 1];
-        const float o = a.ws_o[(base + k) * kHeadDim + d];
+    float Mc = ws_ml[base * 2 + 0];
+    float L = ws_ml[base * 2 + 1];
+    float O = ws_o[base * kHeadDim + d];
+    for (int k = 1; k < n_chunks; ++k) {
+        const float mc = ws_ml[(base + k) * 2 + 0];
+        const float l = ws_ml[(base + k) * 2 + 1];
+        const float o = ws_o[(base + k) * kHeadDim + d];
         float Mcn, A, B;
         fold_scalars(Mc, mc, Mcn, A, B);
         L = __builtin_fmaf(L, A, l * B);
         O = fold_value(O, A, o, B);
         Mc = Mcn;
     }
-    a.o[row * kHeadDim + d] = finalize(O, L);
+    orow[d] = finalize(O, L);
+}
+
+// One workgroup per (batch, query head): copy chunk 0, fold chunks 1.. in
+// order, finalize.
+__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
+    const int64_t row = blockIdx.x;
+    combine_row(a.ws_o, a.ws_ml, row * a.n_chunks, a.n_chunks, a.o + row * kHeadDim);
+}
+
+// Ragged decode: one query token per sequence, q, o [Hq, n_seq_total, 128]
+// packed head-major; caches [Hkv, kv_rows, 128] with sequence s's keys at
+// rows kv_row0[s] .. + kv_len[s] - 1.  Work units of a sequence: (KV head,
+// chunk); its partials start at workspace row ws_row0[s] (Hq * n_chunks rows).
+struct DecodeVarlenTable {
+    int64_t kv_row0[kMaxVarlenSeqs];
+    int64_t ws_row0[kMaxVarlenSeqs];
+    int32_t kv_len[kMaxVarlenSeqs];
+    int32_t seq[kMaxVarlenSeqs];        // the sequence's index among all query tokens
+    int32_t unit0[kMaxVarlenSeqs + 1];  // first work unit of each sequence (prefix sum)
+    int32_t n_seqs;
+};
+
+struct DecodeVarlenArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* ws_o;
+    float* ws_ml;
+    int64_t n_tokens;  // query rows per head (the whole ragged batch)
+    int64_t kv_rows;
+    int32_t n_kv_heads;
+    float c;
+};
+
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_varlen_kernel(DecodeVarlenArgs a, DecodeVarlenTable t) {
+    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * kTileBytes];
+    const int x = blockIdx.x;
+    int s = 0;
+    while (s + 1 < t.n_seqs && t.unit0[s + 1] <= x) ++s;
+    const int64_t kv_len = t.kv_len[s];
+    const int nc = (int)((kv_len + kChunk - 1) / kChunk);
+    const int u = x - t.unit0[s];
+    const int g = u / nc, chunk = u % nc;
+    DecodeWork wk;
+    wk.q = a.q;
+    wk.o = a.o;
+    wk.q_row0 = (int64_t)kGroup * g * a.n_tokens + t.seq[s];
+    wk.q_hstride = a.n_tokens;
+    wk.kbase = a.k + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
+    wk.vbase = a.v + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
+    wk.kv_len = kv_len;
+    wk.chunk = chunk;
+    wk.n_chunks = nc;
+    wk.ws_row0 = t.ws_row0[s] + (int64_t)kGroup * g * nc;
+    decode_body(wk, a.ws_o, a.ws_ml, a.c, smem);
+}
+
+// One workgroup per (sequence with more than one chunk, query head).
+__global__ __launch_bounds__(128) void combine_varlen_kernel(DecodeVarlenArgs a, DecodeVarlenTable t) {
+    const int n_q_heads = kGroup * a.n_kv_heads;
+    const int s = blockIdx.x / n_q_heads, head = blockIdx.x % n_q_heads;
+    const int64_t kv_len = t.kv_len[s];
+    const int nc = (int)((kv_len + kChunk - 1) / kChunk);
+    if (nc == 1) return;
+    combine_row(a.ws_o, a.ws_ml, t.ws_row0[s] + (int64_t)head * nc, nc,
+                a.o + ((int64_t)head * a.n_tokens + t.seq[s]) * kHeadDim);
 }
 
 // ---------------------------------------------------------------------------
@@ -415,6 +586,86 @@ int launch_prefill(bool partitioned, const void* q, const void* k, const void* v
     else
         hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(64 * kPrefillWaves), 0, stream, a);
     return hipGetLastError() == hipSuccess ? KB_ATTN_OK : KB_ATTN_ERR_HIP;
+}
+
+// One sequence of a ragged call, after validation.
+struct RaggedSeq {
+    int64_t index;          // position in the caller's arrays
+    int64_t q_row0, q_len;  // query rows in the packed q / o
+    int64_t kv_row0, kv_len;
+};
+
+// Reads a ragged call's host arrays: query offsets cu_q (batch + 1 entries,
+// non-decreasing), cache offsets cu_kv (same), and, when given, the number of
+// valid keys of each sequence (else the whole cache range).  Checks every
+// sequence against the contract's rules (0 <= q_len <= kv_len <= capacity,
+// and kv_len >= 1 when q_len >= 1) before anything is launched.
+int read_ragged(const int64_t* cu_q, const int64_t* cu_kv, const int64_t* kv_lens, int64_t batch,
+                std::vector<RaggedSeq>& seqs, int64_t& q_rows, int64_t& kv_rows) {
+    if (!cu_q || !cu_kv || batch < 1) return KB_ATTN_ERR_INVALID_ARG;
+    if (cu_q[0] < 0 || cu_kv[0] < 0) return KB_ATTN_ERR_LENGTH;
+    seqs.clear();
+    for (int64_t i = 0; i < batch; ++i) {
+        const int64_t q_len = cu_q[i + 1] - cu_q[i], cap = cu_kv[i + 1] - cu_kv[i];
+        if (q_len < 0 || cap < 0) return KB_ATTN_ERR_LENGTH;
+        const int64_t kv_len = kv_lens ? kv_lens[i] : cap;
+        if (kv_len < 0 || kv_len > cap || q_len > kv_len || cap > kMaxLen) return KB_ATTN_ERR_LENGTH;
+        if (q_len > 0) seqs.push_back({i, cu_q[i], q_len, cu_kv[i], kv_len});
+    }
+    q_rows = cu_q[batch];
+    kv_rows = cu_kv[batch];
+    if (q_rows > kMaxLen * 64 || kv_rows > kMaxLen * 64) return KB_ATTN_ERR_LENGTH;
+    return KB_ATTN_OK;
+}
+
+int launch_prefill_varlen(const void* q, const void* k, const void* v, void* o, std::vector<RaggedSeq> seqs,
+                          int64_t q_rows, int64_t kv_rows, int32_t n_kv_heads, float scale, hipStream_t stream) {
+    // longest sequences first, so the longest position blocks start first
+    std::stable_sort(seqs.begin(), seqs.end(),
+                     [](const RaggedSeq& x, const RaggedSeq& y) { return x.kv_len > y.kv_len; });
+    VarlenArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.o = (uint16_t*)o;
+    a.q_rows = q_rows;
+    a.kv_rows = kv_rows;
+    a.n_kv_heads = n_kv_heads;
+    a.c = contract_c(scale);
+    for (size_t first = 0; first < seqs.size(); first += kMaxVarlenSeqs) {
+        const size_t n = std::min(seqs.size() - first, (size_t)kMaxVarlenSeqs);
+        VarlenTable t;
+        t.n_seqs = (int32_t)n;
+        int64_t units = 0;
+        for (size_t i = 0; i < n; ++i) {
+            const RaggedSeq& sq = seqs[first + i];
+            t.q_row0[i] = sq.q_row0;
+            t.kv_row0[i] = sq.kv_row0;
+            t.q_len[i] = (int32_t)sq.q_len;
+            t.kv_len[i] = (int32_t)sq.kv_len;
+            t.unit0[i] = (int32_t)units;
+            const int64_t n_pb = (sq.kv_len - 1) / 64 - (sq.kv_len - sq.q_len) / 64 + 1;
+            units += n_pb * n_kv_heads;
+            if (units > INT32_MAX) return KB_ATTN_ERR_LENGTH;
+        }
+        t.unit0[n] = (int32_t)units;
+        hipLaunchKernelGGL(prefill_varlen_kernel, dim3((unsigned)units), dim3(64 * kPrefillWaves), 0, stream, a, t);
+        if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+    }
+    return KB_ATTN_OK;
+}
+
+// Workspace rows (one per query head and chunk) of the ragged decode, for the
+// sequences that have more than one chunk; ws_row0 gets each one's first row.
+int64_t ragged_ws_rows(const std::vector<RaggedSeq>& seqs, int32_t n_q_heads, std::vector<int64_t>* ws_row0) {
+    int64_t rows = 0;
+    if (ws_row0) ws_row0->clear();
+    for (const RaggedSeq& sq : seqs) {
+        if (ws_row0) ws_row0->push_back(rows);
+        const int64_t nc = n_chunks_of(sq.kv_len);
+        if (nc > 1) rows += (int64_t)n_q_heads * nc;
+    }
+    return rows;
 }
 
 }  // namespace
@@ -515,6 +766,128 @@ int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
         cmb.c = a.c;
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(kHeadDim), 0, stream, cmb);
         if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+    }
+    return KB_ATTN_OK;
+}
+
+int kb_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, const int64_t* cu_seqlens,
+                           int64_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                           hipStream_t stream) {
+    if (!q || !k || !v || !o || !cu_seqlens || batch < 1) return KB_ATTN_ERR_INVALID_ARG;
+    if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
+    if (int rc = check_scale(scale)) return rc;
+    std::vector<RaggedSeq> seqs;
+    int64_t q_rows = 0, kv_rows = 0;
+    if (int rc = read_ragged(cu_seqlens, cu_seqlens, nullptr, batch, seqs, q_rows, kv_rows)) return rc;
+    if (int rc = check_aligned({q, k, v, o})) return rc;
+    const size_t qbytes = (size_t)n_q_heads * q_rows * kHeadDim * 2;
+    const size_t kvbytes = (size_t)n_kv_heads * kv_rows * kHeadDim * 2;
+    if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k, kvbytes) ||
+        ranges_overlap(o, qbytes, v, kvbytes))
+        return KB_ATTN_ERR_ALIAS;
+    if (int rc = check_device({q, k, v, o})) return rc;
+    return launch_prefill_varlen(q, k, v, o, seqs, q_rows, kv_rows, n_kv_heads, scale, stream);
+}
+
+int kb_attn_partitioned_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, const int64_t* cu_q,
+                               const int64_t* cu_cache, const int64_t* kv_lens, int64_t batch, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, float scale, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !o || !cu_q || !cu_cache || !kv_lens || batch < 1)
+        return KB_ATTN_ERR_INVALID_ARG;
+    if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
+    if (int rc = check_scale(scale)) return rc;
+    std::vector<RaggedSeq> seqs;
+    int64_t q_rows = 0, kv_rows = 0;
+    if (int rc = read_ragged(cu_q, cu_cache, kv_lens, batch, seqs, q_rows, kv_rows)) return rc;
+    if (int rc = check_aligned({q, k_cache, v_cache, o})) return rc;
+    const size_t qbytes = (size_t)n_q_heads * q_rows * kHeadDim * 2;
+    const size_t kvbytes = (size_t)n_kv_heads * kv_rows * kHeadDim * 2;
+    if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k_cache, kvbytes) ||
+        ranges_overlap(o, qbytes, v_cache, kvbytes))
+        return KB_ATTN_ERR_ALIAS;
+    if (int rc = check_device({q, k_cache, v_cache, o})) return rc;
+    return launch_prefill_varlen(q, k_cache, v_cache, o, seqs, q_rows, kv_rows, n_kv_heads, scale, stream);
+}
+
+size_t kb_attn_decode_varlen_workspace_bytes(const int64_t* kv_lens, int64_t batch, int32_t n_q_heads,
+                                             int32_t head_dim) {
+    if (!kv_lens || batch < 1 || n_q_heads < 1 || head_dim != kHeadDim) return 0;
+    int64_t rows = 0;
+    for (int64_t i = 0; i < batch; ++i) {
+        if (kv_lens[i] < 1 || kv_lens[i] > kMaxLen) return 0;
+        const int64_t nc = n_chunks_of(kv_lens[i]);
+        if (nc > 1) rows += (int64_t)n_q_heads * nc;
+    }
+    return (size_t)rows * (kHeadDim + 2) * sizeof(float);
+}
+
+int kb_attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, const int64_t* cu_cache,
+                          const int64_t* kv_lens, int64_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                          int32_t head_dim, float scale, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !o || !cu_cache || !kv_lens || batch < 1) return KB_ATTN_ERR_INVALID_ARG;
+    if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
+    if (int rc = check_scale(scale)) return rc;
+    // one query token per sequence: query offsets 0, 1, ..., batch
+    std::vector<int64_t> cu_tok((size_t)batch + 1);
+    for (int64_t i = 0; i <= batch; ++i) cu_tok[(size_t)i] = i;
+    for (int64_t i = 0; i < batch; ++i)
+        if (kv_lens[i] < 1) return KB_ATTN_ERR_LENGTH;
+    std::vector<RaggedSeq> seqs;
+    int64_t q_rows = 0, kv_rows = 0;
+    if (int rc = read_ragged(cu_tok.data(), cu_cache, kv_lens, batch, seqs, q_rows, kv_rows)) return rc;
+    std::vector<int64_t> ws_row0;
+    const int64_t ws_rows = ragged_ws_rows(seqs, n_q_heads, &ws_row0);
+    const size_t need = (size_t)ws_rows * (kHeadDim + 2) * sizeof(float);
+    if (need && (!workspace || workspace_bytes < need)) return KB_ATTN_ERR_WORKSPACE;
+    if (int rc = check_aligned({q, k_cache, v_cache, o, need ? workspace : nullptr})) return rc;
+    const size_t qbytes = (size_t)n_q_heads * q_rows * kHeadDim * 2;
+    const size_t kvbytes = (size_t)n_kv_heads * kv_rows * kHeadDim * 2;
+    if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k_cache, kvbytes) ||
+        ranges_overlap(o, qbytes, v_cache, kvbytes) || (need && ranges_overlap(o, qbytes, workspace, need)))
+        return KB_ATTN_ERR_ALIAS;
+    if (need && (ranges_overlap(workspace, need, q, qbytes) || ranges_overlap(workspace, need, k_cache, kvbytes) ||
+                 ranges_overlap(workspace, need, v_cache, kvbytes)))
+        return KB_ATTN_ERR_ALIAS;
+    if (int rc = check_device({q, k_cache, v_cache, o, need ? workspace : nullptr})) return rc;
+
+    DecodeVarlenArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k_cache;
+    a.v = (const uint16_t*)v_cache;
+    a.o = (uint16_t*)o;
+    a.ws_o = need ? (float*)workspace : nullptr;
+    a.ws_ml = need ? (float*)workspace + ws_rows * kHeadDim : nullptr;
+    a.n_tokens = batch;
+    a.kv_rows = kv_rows;
+    a.n_kv_heads = n_kv_heads;
+    a.c = contract_c(scale);
+    for (size_t first = 0; first < seqs.size(); first += kMaxVarlenSeqs) {
+        const size_t n = std::min(seqs.size() - first, (size_t)kMaxVarlenSeqs);
+        DecodeVarlenTable t;
+        t.n_seqs = (int32_t)n;
+        int64_t units = 0;
+        bool any_multi = false;
+        for (size_t i = 0; i < n; ++i) {
+            const RaggedSeq& sq = seqs[first + i];
+            t.kv_row0[i] = sq.kv_row0;
+            t.ws_row0[i] = ws_row0[first + i];
+            t.kv_len[i] = (int32_t)sq.kv_len;
+            t.seq[i] = (int32_t)sq.index;
+            t.unit0[i] = (int32_t)units;
+            const int64_t nc = n_chunks_of(sq.kv_len);
+            any_multi = any_multi || nc > 1;
+            units += nc * n_kv_heads;
+            if (units > INT32_MAX) return KB_ATTN_ERR_LENGTH;
+        }
+        t.unit0[n] = (int32_t)units;
+        hipLaunchKernelGGL(decode_varlen_kernel, dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, stream, a, t);
+        if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+        if (any_multi) {
+            hipLaunchKernelGGL(combine_varlen_kernel, dim3((unsigned)(n * n_q_heads)), dim3(kHeadDim), 0, stream, a,
+                               t);
+            if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+        }
     }
     return KB_ATTN_OK;
 }

@@ -107,6 +107,56 @@ int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
 size_t kb_attn_decode_workspace_bytes(int64_t batch, int64_t kv_len, int32_t n_q_heads,
                                       int32_t head_dim);
 
+/*
+ * Ragged (variable-length) batches of the three entry points: the same
+ * contract, row by row, so a sequence's outputs are bit for bit those of the
+ * dense call on that sequence alone.  (Rollout batches mix prompt and answer
+ * lengths; the "Usage" section's prompt/answer splits are per sequence.)
+ *
+ * Packed layout, head-major: a tensor with H heads and R rows per head is
+ * [H, R, 128] contiguous, and sequence i owns rows off[i] .. off[i+1] - 1 of
+ * every head.  The offset and length arrays are HOST arrays (batch + 1
+ * offsets, non-decreasing from >= 0; batch lengths); they are read during the
+ * call, checked in full before anything is launched, and not kept.  Sequences
+ * with no query rows are skipped.  Any batch size is accepted; the work is
+ * issued in launches of at most 64 sequences.
+ */
+
+/* Causal prefill of every sequence: q, o [n_q_heads, cu_seqlens[batch], 128];
+ * k, v [n_kv_heads, cu_seqlens[batch], 128]; row r of sequence i sits at
+ * position r of that sequence. */
+int kb_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
+                           const int64_t* cu_seqlens, int64_t batch, int32_t n_q_heads,
+                           int32_t n_kv_heads, int32_t head_dim, float scale, hipStream_t stream);
+
+/* Partitioned forward of every sequence: q, o [n_q_heads, cu_q[batch], 128];
+ * caches [n_kv_heads, cu_cache[batch], 128].  Sequence i has
+ * q_len = cu_q[i+1] - cu_q[i] query rows, a cache range of capacity
+ * cu_cache[i+1] - cu_cache[i] rows of which the first kv_lens[i] are keys
+ * (0 <= q_len <= kv_len <= capacity, else KB_ATTN_ERR_LENGTH); its row r sits
+ * at position kv_lens[i] - q_len + r. */
+int kb_attn_partitioned_varlen(const void* q, const void* k_cache, const void* v_cache, void* o,
+                               const int64_t* cu_q, const int64_t* cu_cache,
+                               const int64_t* kv_lens, int64_t batch, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, float scale,
+                               hipStream_t stream);
+
+/* One-token decode of every sequence: q, o [n_q_heads, batch, 128] (one row
+ * per sequence); caches as in kb_attn_partitioned_varlen, with
+ * 1 <= kv_lens[i] <= capacity.  Sequences longer than one chunk are split by
+ * chunk; their partials go to `workspace` (device memory, at least
+ * kb_attn_decode_varlen_workspace_bytes(kv_lens, ...) bytes; NULL when that
+ * is 0) and are folded in chunk order. */
+int kb_attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o,
+                          const int64_t* cu_cache, const int64_t* kv_lens, int64_t batch,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes kb_attn_decode_varlen needs for these host kv_lens (0 when
+ * no sequence exceeds one chunk; 0 for invalid arguments). */
+size_t kb_attn_decode_varlen_workspace_bytes(const int64_t* kv_lens, int64_t batch,
+                                             int32_t n_q_heads, int32_t head_dim);
+
 /* Static description of an error code (never NULL). */
 const char* kb_attn_strerror(int code);
 
