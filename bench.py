@@ -228,7 +228,51 @@ def main() -> int:
             nbytes = 4096 * bs * ctx + 16384 * bs
             sweep.append({"batch": bs, "kv_len": ctx, "us_cold": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
                           "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / PEAK_HBM, 4)})
-    del flush
+
+    # ragged batch: 16 sequences of mixed lengths, sequence i = the first L_i
+    # rows of batch i, packed head-major; its rows must equal the dense
+    # prefill's rows bit for bit (row r of batch i sees the same keys 0..r)
+    lens = [16384, 12000, 9000, 7000, 5000, 4096, 3000, 2500, 2049, 1500, 1025, 900, 600, 300, 130, 64]
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    qv = torch.cat([qd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
+    kv_ = torch.cat([kd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
+    vv_ = torch.cat([vd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
+    ov = torch.empty_like(qv)
+    qtok = torch.stack([qv[:, cu[i + 1] - 1] for i in range(len(lens))], dim=1).contiguous()
+    otok = torch.empty_like(qtok)
+    wsv = torch.empty(max(1, kb.decode_varlen_workspace_bytes(lens)), dtype=torch.uint8, device=dev)
+    kb.prefill_varlen(qv, kv_, vv_, cu, out=ov)
+    torch.cuda.synchronize()
+    vt = []
+    for _ in range(5):
+        e0.record(stream)
+        kb.prefill_varlen(qv, kv_, vv_, cu, out=ov)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vt.append(e0.elapsed_time(e1))
+    vd_t = []
+    for _ in range(11):
+        flush.sum()
+        e0.record(stream)
+        kb.decode_varlen(qtok, kv_, vv_, cu, lens, out=otok, workspace=wsv)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vd_t.append(e0.elapsed_time(e1))
+    ov_bits = ov.view(torch.int16)
+    v_mism = sum(int((ov_bits[:, cu[i]:cu[i + 1]] != pre_bits[i, :, :L]).sum()) for i, L in enumerate(lens))
+    v_mism_dec = sum(int((otok.view(torch.int16)[:, i] != ov_bits[:, cu[i + 1] - 1]).sum()) for i in range(len(lens)))
+    v_flops = sum(2 * HQ * D * L * (L + 1) for L in lens)
+    v_ms = float(np.median(vt))
+    v_dec_us = float(np.median(vd_t[1:])) * 1e3
+    v_bytes = sum(4096 * L + 16384 for L in lens)
+    varlen = {"sequences": len(lens), "lengths": lens, "prefill_ms": round(v_ms, 3),
+              "prefill_tflops": round(v_flops / v_ms / 1e9, 2),
+              "prefill_frac_of_peak": round(v_flops / (v_ms * 1e-3) / PEAK_BF16, 4),
+              "decode_us_cold": round(v_dec_us, 2), "decode_gbs": round(v_bytes / v_dec_us / 1e3, 1),
+              "bitwise_mismatch": {"prefill_vs_dense_prefill": v_mism, "decode_vs_prefill": v_mism_dec}}
+    del qv, kv_, vv_, ov, flush
 
     pre_ms = float(np.mean(times["pre"]))
     part_ms = float(np.mean(times["part"]))
@@ -266,6 +310,7 @@ def main() -> int:
                    "ms_cold": round(cold_ms, 4), "gbs_cold": round(dec_bytes / cold_ms / 1e6, 1),
                    "frac_of_peak_cold": round(dec_bytes / (cold_ms * 1e-3) / PEAK_HBM, 4)},
         "decode_sweep": sweep,
+        "varlen": varlen,
         "bitwise_mismatch": {"partitioned_vs_prefill": mism, "decode_vs_prefill": mism_dec},
         "contract": kb.contract(),
         "kernel_source_hash": kernel_source_hash(),
