@@ -112,6 +112,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the decode sweep and the ragged batch (profiling runs: one kernel configuration each)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -207,72 +209,76 @@ def main() -> int:
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
 
-    # decode sweep: batch 1/4/8/16 x context 128/1K/4K/8K over the resident
-    # cache (capacity 16384, first kv_len keys), cold, one query token per head
-    sweep = []
-    for bs in (1, 4, 8, 16):
-        for ctx in (128, 1024, 4096, 8192):
-            qs = qd[:bs, :, ctx - 1:ctx].contiguous()
-            os_ = torch.empty_like(qs)
-            wss = torch.empty(max(1, kb.decode_workspace_bytes(bs, ctx, HQ, D)), dtype=torch.uint8, device=dev)
-            kv_b, vv_b = kd[:bs], vd[:bs]
-            reps = []
-            for i in range(11):
-                flush.sum()
-                e0.record(stream)
-                kb.decode(qs, kv_b, vv_b, kv_len=ctx, out=os_, workspace=wss)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                reps.append(e0.elapsed_time(e1))
-            us = float(np.median(reps[1:])) * 1e3
-            nbytes = 4096 * bs * ctx + 16384 * bs
-            sweep.append({"batch": bs, "kv_len": ctx, "us_cold": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
-                          "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / PEAK_HBM, 4)})
+    sweep, varlen = None, None
+    if not args.no_extras:
+        # decode sweep: batch 1/4/8/16 x context 128/1K/4K/8K over the resident
+        # cache (capacity 16384, first kv_len keys), cold, one query token per head
+        sweep = []
+        for bs in (1, 4, 8, 16):
+            for ctx in (128, 1024, 4096, 8192):
+                qs = qd[:bs, :, ctx - 1:ctx].contiguous()
+                os_ = torch.empty_like(qs)
+                wss = torch.empty(max(1, kb.decode_workspace_bytes(bs, ctx, HQ, D)), dtype=torch.uint8, device=dev)
+                kv_b, vv_b = kd[:bs], vd[:bs]
+                reps = []
+                for i in range(11):
+                    flush.sum()
+                    e0.record(stream)
+                    kb.decode(qs, kv_b, vv_b, kv_len=ctx, out=os_, workspace=wss)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    reps.append(e0.elapsed_time(e1))
+                us = float(np.median(reps[1:])) * 1e3
+                nbytes = 4096 * bs * ctx + 16384 * bs
+                sweep.append({"batch": bs, "kv_len": ctx, "us_cold": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+                              "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / PEAK_HBM, 4)})
 
-    # ragged batch: 16 sequences of mixed lengths, sequence i = the first L_i
-    # rows of batch i, packed head-major; its rows must equal the dense
-    # prefill's rows bit for bit (row r of batch i sees the same keys 0..r)
-    lens = [16384, 12000, 9000, 7000, 5000, 4096, 3000, 2500, 2049, 1500, 1025, 900, 600, 300, 130, 64]
-    cu = [0]
-    for L in lens:
-        cu.append(cu[-1] + L)
-    qv = torch.cat([qd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
-    kv_ = torch.cat([kd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
-    vv_ = torch.cat([vd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
-    ov = torch.empty_like(qv)
-    qtok = torch.stack([qv[:, cu[i + 1] - 1] for i in range(len(lens))], dim=1).contiguous()
-    otok = torch.empty_like(qtok)
-    wsv = torch.empty(max(1, kb.decode_varlen_workspace_bytes(lens)), dtype=torch.uint8, device=dev)
-    kb.prefill_varlen(qv, kv_, vv_, cu, out=ov)
-    torch.cuda.synchronize()
-    vt = []
-    for _ in range(5):
-        e0.record(stream)
+        # ragged batch: 16 sequences of mixed lengths, sequence i = the first L_i
+        # rows of batch i, packed head-major; its rows must equal the dense
+        # prefill's rows bit for bit (row r of batch i sees the same keys 0..r)
+        lens = [16384, 12000, 9000, 7000, 5000, 4096, 3000, 2500, 2049, 1500, 1025, 900, 600, 300, 130, 64]
+        cu = [0]
+        for L in lens:
+            cu.append(cu[-1] + L)
+        qv = torch.cat([qd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
+        kv_ = torch.cat([kd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
+        vv_ = torch.cat([vd[i, :, :L] for i, L in enumerate(lens)], dim=1).contiguous()
+        ov = torch.empty_like(qv)
+        qtok = torch.stack([qv[:, cu[i + 1] - 1] for i in range(len(lens))], dim=1).contiguous()
+        otok = torch.empty_like(qtok)
+        wsv = torch.empty(max(1, kb.decode_varlen_workspace_bytes(lens)), dtype=torch.uint8, device=dev)
         kb.prefill_varlen(qv, kv_, vv_, cu, out=ov)
-        e1.record(stream)
         torch.cuda.synchronize()
-        vt.append(e0.elapsed_time(e1))
-    vd_t = []
-    for _ in range(11):
-        flush.sum()
-        e0.record(stream)
-        kb.decode_varlen(qtok, kv_, vv_, cu, lens, out=otok, workspace=wsv)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        vd_t.append(e0.elapsed_time(e1))
-    ov_bits = ov.view(torch.int16)
-    v_mism = sum(int((ov_bits[:, cu[i]:cu[i + 1]] != pre_bits[i, :, :L]).sum()) for i, L in enumerate(lens))
-    v_mism_dec = sum(int((otok.view(torch.int16)[:, i] != ov_bits[:, cu[i + 1] - 1]).sum()) for i in range(len(lens)))
-    v_flops = sum(2 * HQ * D * L * (L + 1) for L in lens)
-    v_ms = float(np.median(vt))
-    v_dec_us = float(np.median(vd_t[1:])) * 1e3
-    v_bytes = sum(4096 * L + 16384 for L in lens)
-    varlen = {"sequences": len(lens), "lengths": lens, "prefill_ms": round(v_ms, 3),
-              "prefill_tflops": round(v_flops / v_ms / 1e9, 2),
-              "prefill_frac_of_peak": round(v_flops / (v_ms * 1e-3) / PEAK_BF16, 4),
-              "decode_us_cold": round(v_dec_us, 2), "decode_gbs": round(v_bytes / v_dec_us / 1e3, 1),
-              "bitwise_mismatch": {"prefill_vs_dense_prefill": v_mism, "decode_vs_prefill": v_mism_dec}}
-    del qv, kv_, vv_, ov, flush
+        vt = []
+        for _ in range(5):
+            e0.record(stream)
+            kb.prefill_varlen(qv, kv_, vv_, cu, out=ov)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            vt.append(e0.elapsed_time(e1))
+        vd_t = []
+        for _ in range(11):
+            flush.sum()
+            e0.record(stream)
+            kb.decode_varlen(qtok, kv_, vv_, cu, lens, out=otok, workspace=wsv)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            vd_t.append(e0.elapsed_time(e1))
+        ov_bits = ov.view(torch.int16)
+        v_mism = sum(int((ov_bits[:, cu[i]:cu[i + 1]] != pre_bits[i, :, :L]).sum()) for i, L in enumerate(lens))
+        v_mism_dec = sum(int((otok.view(torch.int16)[:, i] != ov_bits[:, cu[i + 1] - 1]).sum())
+                         for i in range(len(lens)))
+        v_flops = sum(2 * HQ * D * L * (L + 1) for L in lens)
+        v_ms = float(np.median(vt))
+        v_dec_us = float(np.median(vd_t[1:])) * 1e3
+        v_bytes = sum(4096 * L + 16384 for L in lens)
+        varlen = {"sequences": len(lens), "lengths": lens, "prefill_ms": round(v_ms, 3),
+                  "prefill_tflops": round(v_flops / v_ms / 1e9, 2),
+                  "prefill_frac_of_peak": round(v_flops / (v_ms * 1e-3) / PEAK_BF16, 4),
+                  "decode_us_cold": round(v_dec_us, 2), "decode_gbs": round(v_bytes / v_dec_us / 1e3, 1),
+                  "bitwise_mismatch": {"prefill_vs_dense_prefill": v_mism, "decode_vs_prefill": v_mism_dec}}
+        del qv, kv_, vv_, ov
+    del flush
 
     pre_ms = float(np.mean(times["pre"]))
     part_ms = float(np.mean(times["part"]))

@@ -1,12 +1,12 @@
 """Turn rocprofv3 output of bench.py into the short summaries kept in profiles/.
 
 The GPU runs (each command runs committed files only):
-  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline
-  rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
-  rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
+  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras
+  rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras
+  rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras
   rocprofv3 --pmc FETCH_SIZE -d <copy_fetch> -o run --output-format csv -- python3 bench.py --copy-probe
   rocprofv3 --pmc WRITE_SIZE -d <copy_write> -o run --output-format csv -- python3 bench.py --copy-probe
-  rocprofv3 --pmc <8 SQ counters> -d <sqN> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
+  rocprofv3 --pmc <8 SQ counters> -d <sqN> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras
       (two passes, SQ_PASSES below)
 Then, on any host:
   python bench_profile.py --stats <stats> --fetch <fetch> --write <write> \
@@ -88,7 +88,7 @@ def sq_summary(dirs, out: str, src_hash: str) -> None:
              f"kernel source hash (code without comments): {src_hash}", "",
              "commands (one pass each, counters split to stay within the SQ block limit):"]
     lines += [f"  rocprofv3 --pmc {p} -d <dir> -o run --output-format csv -- "
-              "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline" for p in SQ_PASSES]
+              "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras" for p in SQ_PASSES]
     lines += ["", "values for the full-prefill dispatch (SQ_WAVE_CYCLES and SQ_ACTIVE_* are in 4-cycle units):"]
     lines += [f"  {k:<32} {v:>12.4g}   per wave per 64-key tile {v / tiles:>9.2f}" for k, v in sorted(vals.items())]
     if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "SQ_BUSY_CU_CYCLES" in vals:
@@ -139,11 +139,11 @@ def main():
             "",
             "commands:",
             "  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras",
             "  rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- "
-            "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+            "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras",
             "  rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- "
-            "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+            "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras",
             "  rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE ... -- python3 bench.py --copy-probe   (1 GiB copy)",
             "  python bench_profile.py --stats <stats> --fetch <fetch> --write <write> "
             "--copy-fetch <copy_fetch> --copy-write <copy_write> --out profiles",
