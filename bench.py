@@ -209,7 +209,7 @@ def main() -> int:
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
 
-    sweep, varlen = None, None
+    sweep, varlen, paged = None, None, None
     if not args.no_extras:
         # decode sweep: batch 1/4/8/16 x context 128/1K/4K/8K over the resident
         # cache (capacity 16384, first kv_len keys), cold, one query token per head
@@ -278,6 +278,39 @@ def main() -> int:
                   "decode_us_cold": round(v_dec_us, 2), "decode_gbs": round(v_bytes / v_dec_us / 1e3, 1),
                   "bitwise_mismatch": {"prefill_vs_dense_prefill": v_mism, "decode_vs_prefill": v_mism_dec}}
         del qv, kv_, vv_, ov
+
+        # paged decode: the same B=16, context-8192 decode over 64-key pages in
+        # shuffled pool order; must give the dense decode's bits
+        ps = 64
+        npg = DEC_LEN // ps
+
+        def to_pool(x):
+            logical = x[:, :, :DEC_LEN].reshape(B, HKV, npg, ps, D).permute(0, 2, 1, 3, 4).reshape(B * npg, HKV, ps, D)
+            pool = torch.empty_like(logical)
+            pool[perm] = logical
+            return pool
+
+        perm = torch.randperm(B * npg, generator=torch.Generator().manual_seed(7)).to(dev)
+        kpool, vpool = to_pool(kd), to_pool(vd)
+        table = perm.view(B, npg).to(torch.int32).contiguous()
+        qpg = q_dec.view(B, HQ, D)
+        opg = torch.empty_like(qpg)
+        wsp = torch.empty(max(1, kb.decode_varlen_workspace_bytes([DEC_LEN] * B)), dtype=torch.uint8, device=dev)
+        pt = []
+        for _ in range(11):
+            flush.sum()
+            e0.record(stream)
+            kb.decode_paged(qpg, kpool, vpool, table, [DEC_LEN] * B, out=opg, workspace=wsp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pt.append(e0.elapsed_time(e1))
+        p_us = float(np.median(pt[1:])) * 1e3
+        paged = {"batch": B, "kv_len": DEC_LEN, "page_size": ps, "us_cold": round(p_us, 2),
+                 "gbs": round(dec_bytes / p_us / 1e3, 1),
+                 "frac_of_hbm_peak": round(dec_bytes / (p_us * 1e-6) / PEAK_HBM, 4),
+                 "bitwise_mismatch_vs_dense_decode": int((opg.view(torch.int16)
+                                                          != out_dec.view(B, HQ, D).view(torch.int16)).sum())}
+        del kpool, vpool
     del flush
 
     pre_ms = float(np.mean(times["pre"]))
@@ -317,6 +350,7 @@ def main() -> int:
                    "frac_of_peak_cold": round(dec_bytes / (cold_ms * 1e-3) / PEAK_HBM, 4)},
         "decode_sweep": sweep,
         "varlen": varlen,
+        "paged_decode": paged,
         "bitwise_mismatch": {"partitioned_vs_prefill": mism, "decode_vs_prefill": mism_dec},
         "contract": kb.contract(),
         "kernel_source_hash": kernel_source_hash(),

@@ -13,6 +13,7 @@ Entry points (KernelBraid / AReaL-TIK README, "Usage" and "Method"):
   unified_prefill / unified_decode          the README's call shapes
   prefill_varlen / partitioned_varlen / decode_varlen
                                             ragged batches, packed [heads, rows, 128]
+  decode_paged                              decode over a paged KV cache
 All of them give bitwise-identical rows for the same inputs and context.
 """
 from __future__ import annotations
@@ -63,6 +64,9 @@ def lib() -> ctypes.CDLL:
         L.kb_attn_decode_varlen.argtypes = [vp, vp, vp, vp, p64, p64, i64, i32, i32, i32, f32, vp, ctypes.c_size_t,
                                             vp]
         L.kb_attn_decode_varlen.restype = ctypes.c_int
+        L.kb_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i64, p64, i64, i64, i32, i32, i32, i32, f32, vp,
+                                           ctypes.c_size_t, vp]
+        L.kb_attn_decode_paged.restype = ctypes.c_int
         L.kb_attn_decode_varlen_workspace_bytes.argtypes = [p64, i64, i32, i32]
         L.kb_attn_decode_varlen_workspace_bytes.restype = ctypes.c_size_t
         L.kb_attn_strerror.argtypes = [ctypes.c_int]
@@ -245,6 +249,38 @@ def decode_varlen(q, k_cache, v_cache, cu_cache, kv_lens, scale: float | None = 
     check(lib().kb_attn_decode_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), a_c,
                                       a_l, batch, q.shape[0], k_cache.shape[0], HEAD_DIM, _scale(scale, HEAD_DIM),
                                       ws_ptr, ws_bytes, _stream(q)))
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float | None = None, out=None, workspace=None):
+    """One-token decode over a paged cache.  q [B, Hq, 128]; pools [n_pages,
+    Hkv, page_size, 128]; block_table int32 [B, max_pages] on the GPU; kv_lens
+    a host list.  Key j of sequence i is row j % page_size of page
+    block_table[i, j // page_size]."""
+    torch = _torch()
+    _check_tensor("q", q, ndim=3)
+    _check_tensor("k_pages", k_pages)
+    _check_tensor("v_pages", v_pages)
+    if k_pages.shape != v_pages.shape or k_pages.shape[3] != HEAD_DIM or q.shape[2] != HEAD_DIM:
+        raise ValueError("page pools must be [n_pages, Hkv, page_size, 128] and q [B, Hq, 128]")
+    if (not isinstance(block_table, torch.Tensor) or block_table.dtype != torch.int32 or not block_table.is_cuda
+            or block_table.dim() != 2 or not block_table.is_contiguous() or block_table.shape[0] != q.shape[0]):
+        raise ValueError("block_table must be a contiguous int32 [B, max_pages] tensor on the GPU")
+    B, Hq = q.shape[0], q.shape[1]
+    if len(kv_lens) != B:
+        raise ValueError("kv_lens must have one entry per sequence")
+    need = decode_varlen_workspace_bytes(kv_lens, Hq)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a_l = _host_i64(kv_lens)
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, ndim=3)
+    check(lib().kb_attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
+                                     block_table.data_ptr(), block_table.shape[1], a_l, B, k_pages.shape[0],
+                                     k_pages.shape[2], Hq, k_pages.shape[1], HEAD_DIM, _scale(scale, HEAD_DIM), ws_ptr,
+                                     ws_bytes, _stream(q)))
     return out
 
 

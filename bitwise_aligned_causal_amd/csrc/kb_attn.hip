@@ -295,12 +295,23 @@ struct DecodeWork {
     int64_t kv_len;
     int chunk, n_chunks;
     int64_t ws_row0;  // partial of query head 4g + i, this chunk: ws row ws_row0 + i * n_chunks + chunk
+    // paged caches only: this sequence's row of the block table and the pool
+    const int32_t* pages;
+    const uint16_t* kpool;
+    const uint16_t* vpool;
+    int64_t page_elems;  // elements of one page (all KV heads)
+    int64_t head_elems;  // offset of this KV head inside a page
+    int32_t page_size, n_pages;
 };
 
 // Workgroup = 4 waves on one (sequence, KV head, chunk).  The four query heads
 // sit in MFMA columns 0..3 (the other columns hold zeros).  Every wave computes
 // the scores of the tile; wave w accumulates the output rows d = 32w..32w+31.
-// The chunk's tiles stream through a kDecodeStages-deep LDS ring.
+// The chunk's tiles stream through a kDecodeStages-deep LDS ring.  With kPaged
+// the keys come from a paged cache: a page holds page_size (a multiple of 64)
+// consecutive keys, so every 64-key tile lies inside one page; page indices
+// are clamped to the pool, so no table entry can make a load leave it.
+template <bool kPaged>
 __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, float* ws_ml, float c, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -317,15 +328,33 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
     const int t0 = chunk * kTilesPerChunk;
     const int t1 = min(t0 + kTilesPerChunk, n_tiles);
 
-    // ring of kDecodeStages tiles, loads kDecodeStages - 1 tiles ahead
     StagePlan<kDecodeWaves> plan;
     stage_plan(plan, lane, w);
+
+    // paged: lane i holds the pool index of the chunk's i-th page (at most 16)
+    int pg = 0, p0 = 0;
+    if (kPaged) {
+        p0 = (int)((int64_t)t0 * kTile / wk.page_size);
+        const int p1 = (int)((min((int64_t)t1 * kTile, kv_len) - 1) / wk.page_size);
+        pg = lane <= p1 - p0 ? wk.pages[p0 + lane] : 0;
+        pg = min(max(pg, 0), wk.n_pages - 1);
+    }
+    auto stage = [&](int t, char* nb) {
+        if (kPaged) {
+            const int64_t key0 = (int64_t)t * kTile;
+            const int page = __builtin_amdgcn_readlane(pg, (int)(key0 / wk.page_size) - p0);
+            const int64_t off = (int64_t)page * wk.page_elems + wk.head_elems + (key0 % wk.page_size) * kHeadDim;
+            stage_tile(plan, wk.kpool + off, wk.vpool + off, 0, min((int64_t)kTile, kv_len - key0), nb, nb + kKBytes,
+                       lane, w);
+        } else {
+            stage_tile(plan, kbase, vbase, (int64_t)t * kTile, kv_len, nb, nb + kKBytes, lane, w);
+        }
+    };
+
+    // ring of kDecodeStages tiles, loads kDecodeStages - 1 tiles ahead
 #pragma unroll
     for (int i = 0; i < kDecodeStages - 1; ++i) {
-        if (t0 + i < t1) {
-            char* nb = smem + i * kTileBytes;
-            stage_tile(plan, kbase, vbase, (int64_t)(t0 + i) * kTile, kv_len, nb, nb + kKBytes, lane, w);
-        }
+        if (t0 + i < t1) stage(t0 + i, smem + i * kTileBytes);
     }
 
     const int64_t qrow_idx = wk.q_row0 + (int64_t)hi * wk.q_hstride;
@@ -348,11 +377,8 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
         const int ahead = min(t1 - 1, t + kDecodeStages - 2) - t;
         wait_tiles_decode(ahead);
         __syncthreads();
-        if (t + kDecodeStages - 1 < t1) {
-            char* nb = smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * kTileBytes;
-            stage_tile(plan, kbase, vbase, (int64_t)(t + kDecodeStages - 1) * kTile, kv_len, nb, nb + kKBytes,
-                       lane, w);
-        }
+        if (t + kDecodeStages - 1 < t1)
+            stage(t + kDecodeStages - 1, smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * kTileBytes);
         const char* buf = smem + ((t - t0) % kDecodeStages) * kTileBytes;
         // only the context's last tile can hold keys beyond kv_len - 1
         if (t < n_tiles - 1)
@@ -413,7 +439,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     wk.chunk = chunk;
     wk.n_chunks = a.n_chunks;
     wk.ws_row0 = wk.q_row0 * a.n_chunks;
-    decode_body(wk, a.ws_o, a.ws_ml, a.c, smem);
+    decode_body<false>(wk, a.ws_o, a.ws_ml, a.c, smem);
 }
 
 struct CombineArgs {
@@ -467,17 +493,21 @@ struct DecodeVarlenTable {
 
 struct DecodeVarlenArgs {
     const uint16_t* q;
-    const uint16_t* k;
+    const uint16_t* k;  // packed caches, or the page pools (paged)
     const uint16_t* v;
     uint16_t* o;
     float* ws_o;
     float* ws_ml;
-    int64_t n_tokens;  // query rows per head (the whole ragged batch)
-    int64_t kv_rows;
+    int64_t tok_stride, head_stride;  // query / output row of (sequence s, head h): s * tok_stride + h * head_stride
+    int64_t kv_rows;                  // packed caches: rows per KV head
+    const int32_t* block_table;       // paged: [sequences, max_pages] pool indices
+    int64_t max_pages;
+    int32_t page_size, n_pages;
     int32_t n_kv_heads;
     float c;
 };
 
+template <bool kPaged>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_varlen_kernel(DecodeVarlenArgs a, DecodeVarlenTable t) {
     __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * kTileBytes];
     const int x = blockIdx.x;
@@ -490,15 +520,26 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_varlen_kernel(Decode
     DecodeWork wk;
     wk.q = a.q;
     wk.o = a.o;
-    wk.q_row0 = (int64_t)kGroup * g * a.n_tokens + t.seq[s];
-    wk.q_hstride = a.n_tokens;
-    wk.kbase = a.k + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
-    wk.vbase = a.v + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
+    wk.q_row0 = (int64_t)t.seq[s] * a.tok_stride + (int64_t)kGroup * g * a.head_stride;
+    wk.q_hstride = a.head_stride;
+    if (kPaged) {
+        wk.kbase = wk.vbase = nullptr;
+        wk.pages = a.block_table + (int64_t)t.seq[s] * a.max_pages;
+        wk.kpool = a.k;
+        wk.vpool = a.v;
+        wk.page_elems = (int64_t)a.n_kv_heads * a.page_size * kHeadDim;
+        wk.head_elems = (int64_t)g * a.page_size * kHeadDim;
+        wk.page_size = a.page_size;
+        wk.n_pages = a.n_pages;
+    } else {
+        wk.kbase = a.k + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
+        wk.vbase = a.v + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
+    }
     wk.kv_len = kv_len;
     wk.chunk = chunk;
     wk.n_chunks = nc;
     wk.ws_row0 = t.ws_row0[s] + (int64_t)kGroup * g * nc;
-    decode_body(wk, a.ws_o, a.ws_ml, a.c, smem);
+    decode_body<kPaged>(wk, a.ws_o, a.ws_ml, a.c, smem);
 }
 
 // One workgroup per (sequence with more than one chunk, query head).
@@ -509,7 +550,7 @@ __global__ __launch_bounds__(128) void combine_varlen_kernel(DecodeVarlenArgs a,
     const int nc = (int)((kv_len + kChunk - 1) / kChunk);
     if (nc == 1) return;
     combine_row(a.ws_o, a.ws_ml, t.ws_row0[s] + (int64_t)head * nc, nc,
-                a.o + ((int64_t)head * a.n_tokens + t.seq[s]) * kHeadDim);
+                a.o + ((int64_t)t.seq[s] * a.tok_stride + (int64_t)head * a.head_stride) * kHeadDim);
 }
 
 // ---------------------------------------------------------------------------
@@ -666,6 +707,45 @@ int64_t ragged_ws_rows(const std::vector<RaggedSeq>& seqs, int32_t n_q_heads, st
         if (nc > 1) rows += (int64_t)n_q_heads * nc;
     }
     return rows;
+}
+
+// Issue a ragged or paged decode: launches of at most kMaxVarlenSeqs
+// sequences, each followed by its combine when a sequence has several chunks.
+int launch_decode_tables(const DecodeVarlenArgs& a, const std::vector<RaggedSeq>& seqs,
+                         const std::vector<int64_t>& ws_row0, int32_t n_q_heads, bool paged, hipStream_t stream) {
+    for (size_t first = 0; first < seqs.size(); first += kMaxVarlenSeqs) {
+        const size_t n = std::min(seqs.size() - first, (size_t)kMaxVarlenSeqs);
+        DecodeVarlenTable t;
+        t.n_seqs = (int32_t)n;
+        int64_t units = 0;
+        bool any_multi = false;
+        for (size_t i = 0; i < n; ++i) {
+            const RaggedSeq& sq = seqs[first + i];
+            t.kv_row0[i] = sq.kv_row0;
+            t.ws_row0[i] = ws_row0[first + i];
+            t.kv_len[i] = (int32_t)sq.kv_len;
+            t.seq[i] = (int32_t)sq.index;
+            t.unit0[i] = (int32_t)units;
+            const int64_t nc = n_chunks_of(sq.kv_len);
+            any_multi = any_multi || nc > 1;
+            units += nc * a.n_kv_heads;
+            if (units > INT32_MAX) return KB_ATTN_ERR_LENGTH;
+        }
+        t.unit0[n] = (int32_t)units;
+        if (paged)
+            hipLaunchKernelGGL(decode_varlen_kernel<true>, dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, stream, a,
+                               t);
+        else
+            hipLaunchKernelGGL(decode_varlen_kernel<false>, dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, stream,
+                               a, t);
+        if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+        if (any_multi) {
+            hipLaunchKernelGGL(combine_varlen_kernel, dim3((unsigned)(n * n_q_heads)), dim3(kHeadDim), 0, stream, a,
+                               t);
+            if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+        }
+    }
+    return KB_ATTN_OK;
 }
 
 }  // namespace
@@ -858,38 +938,70 @@ int kb_attn_decode_varlen(const void* q, const void* k_cache, const void* v_cach
     a.o = (uint16_t*)o;
     a.ws_o = need ? (float*)workspace : nullptr;
     a.ws_ml = need ? (float*)workspace + ws_rows * kHeadDim : nullptr;
-    a.n_tokens = batch;
+    a.tok_stride = 1;
+    a.head_stride = batch;
     a.kv_rows = kv_rows;
+    a.block_table = nullptr;
+    a.max_pages = 0;
+    a.page_size = 0;
+    a.n_pages = 0;
     a.n_kv_heads = n_kv_heads;
     a.c = contract_c(scale);
-    for (size_t first = 0; first < seqs.size(); first += kMaxVarlenSeqs) {
-        const size_t n = std::min(seqs.size() - first, (size_t)kMaxVarlenSeqs);
-        DecodeVarlenTable t;
-        t.n_seqs = (int32_t)n;
-        int64_t units = 0;
-        bool any_multi = false;
-        for (size_t i = 0; i < n; ++i) {
-            const RaggedSeq& sq = seqs[first + i];
-            t.kv_row0[i] = sq.kv_row0;
-            t.ws_row0[i] = ws_row0[first + i];
-            t.kv_len[i] = (int32_t)sq.kv_len;
-            t.seq[i] = (int32_t)sq.index;
-            t.unit0[i] = (int32_t)units;
-            const int64_t nc = n_chunks_of(sq.kv_len);
-            any_multi = any_multi || nc > 1;
-            units += nc * n_kv_heads;
-            if (units > INT32_MAX) return KB_ATTN_ERR_LENGTH;
-        }
-        t.unit0[n] = (int32_t)units;
-        hipLaunchKernelGGL(decode_varlen_kernel, dim3((unsigned)units), dim3(64 * kDecodeWaves), 0, stream, a, t);
-        if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
-        if (any_multi) {
-            hipLaunchKernelGGL(combine_varlen_kernel, dim3((unsigned)(n * n_q_heads)), dim3(kHeadDim), 0, stream, a,
-                               t);
-            if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
-        }
+    return launch_decode_tables(a, seqs, ws_row0, n_q_heads, false, stream);
+}
+
+int kb_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o,
+                         const int32_t* block_table, int64_t max_pages, const int64_t* kv_lens, int64_t batch,
+                         int64_t n_pages, int32_t page_size, int32_t n_q_heads, int32_t n_kv_heads,
+                         int32_t head_dim, float scale, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (!q || !k_pages || !v_pages || !o || !block_table || !kv_lens || batch < 1 || max_pages < 1 || n_pages < 1)
+        return KB_ATTN_ERR_INVALID_ARG;
+    if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
+    if (int rc = check_scale(scale)) return rc;
+    if (page_size < kTile || page_size % kTile != 0) return KB_ATTN_ERR_UNSUPPORTED;
+    if (n_pages > INT32_MAX || max_pages * page_size > kMaxLen || batch > INT32_MAX) return KB_ATTN_ERR_LENGTH;
+    std::vector<RaggedSeq> seqs;
+    for (int64_t i = 0; i < batch; ++i) {
+        if (kv_lens[i] < 1 || kv_lens[i] > max_pages * page_size) return KB_ATTN_ERR_LENGTH;
+        seqs.push_back({i, i, 1, 0, kv_lens[i]});
     }
-    return KB_ATTN_OK;
+    std::vector<int64_t> ws_row0;
+    const int64_t ws_rows = ragged_ws_rows(seqs, n_q_heads, &ws_row0);
+    const size_t need = (size_t)ws_rows * (kHeadDim + 2) * sizeof(float);
+    if (need && (!workspace || workspace_bytes < need)) return KB_ATTN_ERR_WORKSPACE;
+    if (int rc = check_aligned({q, k_pages, v_pages, o, need ? workspace : nullptr})) return rc;
+    if ((uintptr_t)block_table & 3u) return KB_ATTN_ERR_ALIGNMENT;
+    const size_t qbytes = (size_t)batch * n_q_heads * kHeadDim * 2;
+    const size_t poolbytes = (size_t)n_pages * n_kv_heads * page_size * kHeadDim * 2;
+    const size_t tbytes = (size_t)batch * max_pages * sizeof(int32_t);
+    if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k_pages, poolbytes) ||
+        ranges_overlap(o, qbytes, v_pages, poolbytes) || ranges_overlap(o, qbytes, block_table, tbytes) ||
+        (need && ranges_overlap(o, qbytes, workspace, need)))
+        return KB_ATTN_ERR_ALIAS;
+    if (need && (ranges_overlap(workspace, need, q, qbytes) || ranges_overlap(workspace, need, k_pages, poolbytes) ||
+                 ranges_overlap(workspace, need, v_pages, poolbytes) ||
+                 ranges_overlap(workspace, need, block_table, tbytes)))
+        return KB_ATTN_ERR_ALIAS;
+    if (int rc = check_device({q, k_pages, v_pages, o, block_table, need ? workspace : nullptr})) return rc;
+
+    DecodeVarlenArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k_pages;
+    a.v = (const uint16_t*)v_pages;
+    a.o = (uint16_t*)o;
+    a.ws_o = need ? (float*)workspace : nullptr;
+    a.ws_ml = need ? (float*)workspace + ws_rows * kHeadDim : nullptr;
+    a.tok_stride = n_q_heads;  // q, o [batch, n_q_heads, 128]
+    a.head_stride = 1;
+    a.kv_rows = 0;
+    a.block_table = block_table;
+    a.max_pages = max_pages;
+    a.page_size = page_size;
+    a.n_pages = (int32_t)n_pages;
+    a.n_kv_heads = n_kv_heads;
+    a.c = contract_c(scale);
+    return launch_decode_tables(a, seqs, ws_row0, n_q_heads, true, stream);
 }
 
 const char* kb_attn_strerror(int code) {

@@ -157,6 +157,31 @@ int kb_attn_decode_varlen(const void* q, const void* k_cache, const void* v_cach
 size_t kb_attn_decode_varlen_workspace_bytes(const int64_t* kv_lens, int64_t batch,
                                              int32_t n_q_heads, int32_t head_dim);
 
+/*
+ * One-token decode over a paged KV cache, the layout rollout engines keep
+ * (an extension the pages leave open: "Method" lets data movement vary
+ * inside the contract).  Output bits equal those of kb_attn_decode on the
+ * same keys laid out contiguously.
+ *   q, o         [batch, n_q_heads, 128] (DEVICE, as kb_attn_decode's q, o)
+ *   k_pages,
+ *   v_pages      page pools [n_pages, n_kv_heads, page_size, 128] (DEVICE);
+ *                page_size must be a multiple of 64 (KB_ATTN_ERR_UNSUPPORTED),
+ *                so every 64-key tile lies inside one page
+ *   block_table  int32 [batch, max_pages] (DEVICE, 4-byte aligned): key j of
+ *                sequence i is row j % page_size of page
+ *                block_table[i * max_pages + j / page_size]; entries outside
+ *                [0, n_pages) are clamped into the pool (no access leaves it;
+ *                the output of such a sequence is then unspecified)
+ *   kv_lens      HOST int64 [batch], 1 <= kv_lens[i] <= max_pages * page_size
+ *   workspace    as kb_attn_decode_varlen (size it with
+ *                kb_attn_decode_varlen_workspace_bytes(kv_lens, ...)).
+ */
+int kb_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o,
+                         const int32_t* block_table, int64_t max_pages, const int64_t* kv_lens,
+                         int64_t batch, int64_t n_pages, int32_t page_size, int32_t n_q_heads,
+                         int32_t n_kv_heads, int32_t head_dim, float scale, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of an error code (never NULL). */
 const char* kb_attn_strerror(int code);
 

@@ -95,3 +95,28 @@ def test_binding_checks_offsets_against_tensors():
     q = torch.zeros(32, 10, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         kb.prefill_varlen(q, q[:8], q[:8], [0, 5, 10])  # CPU tensors are refused
+
+
+def paged(lens=(100, 3000), page_size=64, max_pages=64, n_pages=200, table=None, ws=W, ws_bytes=1 << 24, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, hq=32, hkv=8, d=128, scale=SCALE, batch=len(lens), kl=arr(list(lens)),
+             table=ctypes.c_void_p(0x20_0000_0000) if table is None else table)
+    a.update(kw)
+    return kb.lib().kb_attn_decode_paged(a["q"], a["k"], a["v"], a["o"], a["table"], max_pages, a["kl"], a["batch"],
+                                         n_pages, page_size, a["hq"], a["hkv"], a["d"], a["scale"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(table=ctypes.c_void_p(0)), INVALID), (dict(kl=None), INVALID),
+    (dict(batch=0), INVALID), (dict(max_pages=0), INVALID), (dict(n_pages=0), INVALID),
+    (dict(page_size=32), UNSUPPORTED), (dict(page_size=100), UNSUPPORTED), (dict(d=64), UNSUPPORTED),
+    (dict(lens=(0, 10)), LENGTH), (dict(lens=(64 * 64 + 1, 10)), LENGTH),
+    (dict(table=ctypes.c_void_p(0x20_0000_0002)), ALIGN), (dict(q=ctypes.c_void_p(Q.value + 4)), ALIGN),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+    (dict(o=Q), ALIAS), (dict(o=ctypes.c_void_p(0x20_0000_0000)), ALIAS),
+])
+def test_paged_rejected_before_launch(kw, expect):
+    base = dict(lens=(100, 3000), page_size=64, max_pages=64, n_pages=200)
+    for key in list(kw):
+        if key in base:
+            base[key] = kw.pop(key)
+    assert paged(**base, **kw) == expect
