@@ -81,9 +81,55 @@ def battery(entry) -> bool:
 
 
 def test_unmodified_copy_passes(tmp_path):
-    assert battery(build_variant(tmp_path, "clean", []))
+    entry = build_variant(tmp_path, "clean", [])
+    assert battery(entry)
+    assert bwd_battery(entry)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(tmp_path, name):
     assert not battery(build_variant(tmp_path, name, MUTANTS[name])), f"pins missed mutant {name}"
+
+
+# Mistakes planted in the log-sum-exp and the backward; caught by the
+# backward pins of test_oracle_bwd_pins.py.
+BWD_MUTANTS = {
+    "lse_drops_max": [("if (lse) *lse = m + kbo_log(l);", "if (lse) *lse = kbo_log(l);")],
+    "ds_drops_d_term": [("ds[j] = (real)w[j] * (dp - Di);", "ds[j] = (real)w[j] * dp;")],
+    "ds_sign": [("ds[j] = (real)w[j] * (dp - Di);", "ds[j] = (real)w[j] * (Di - dp);")],
+    "dp_reads_k": [("const uint16_t* vrows = p->v + (b * p->n_kv_heads + g) * S * D;",
+                    "const uint16_t* vrows = p->k + (b * p->n_kv_heads + g) * S * D;")],
+    "dv_uses_q": [("if (dvb) dvb[j * D + d] += (double)((real)w[j] * dod);",
+                   "if (dvb) dvb[j * D + d] += (double)((real)w[j] * qd);")],
+    "dk_unscaled": [("if (dkb) dkb[j * D + d] += (double)(p->scale * ds[j] * qd);",
+                     "if (dkb) dkb[j * D + d] += (double)(ds[j] * qd);")],
+    "dq_reversed_channels": [("acc += ds[j] * widen(krows[j * D + d]);",
+                              "acc += ds[j] * widen(krows[j * D + (D - 1 - d)]);")],
+    "d_uses_v0": [("for (int64_t d = 0; d < D; ++d) Di += widen(dorow[d]) * o[d];",
+                   "for (int64_t d = 0; d < D; ++d) Di += widen(dorow[d]) * widen(vrows[d]);")],
+    "dk_to_wrong_group": [("b = x / Hkv;\n            g = x % Hkv;\n            h_first = g * hpg;",
+                           "b = x / Hkv;\n            g = x % Hkv;\n            h_first = ((g + 1) % Hkv) * hpg;")],
+}
+
+
+def bwd_battery(entry) -> bool:
+    """True when the build passes the backward and log-sum-exp pins."""
+    import test_oracle_bwd_pins as bp
+
+    ok = True
+    for shape in [(2, 4, 2, 7, 8), (1, 8, 2, 17, 16)]:
+        B, Hq, Hkv, S, D = shape
+        q, k, v, do = bp.grads_inputs(211 + sum(shape), B, Hq, Hkv, S, D)
+        scale = 1.0 / math.sqrt(D)
+        ref = bp.sdpa_autograd(q, k, v, do, scale)
+        got = oracle.backward(q, k, v, do, scale=scale, entry=entry)
+        for name, r in zip(("dq", "dk", "dv"), ref):
+            ok &= bool(np.allclose(got[name], r, rtol=0, atol=1e-11 * max(1.0, np.abs(r).max())))
+        lref = bp.masked_lse_torch(q, k, S, scale)
+        ok &= bool(np.allclose(oracle.lse(q, k, v, scale=scale, entry=entry), lref, rtol=0, atol=1e-12))
+    return ok
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_mutant_is_caught(tmp_path, name):
+    assert not bwd_battery(build_variant(tmp_path, name, BWD_MUTANTS[name])), f"pins missed mutant {name}"
