@@ -14,7 +14,12 @@ Entry points (KernelBraid / AReaL-TIK README, "Usage" and "Method"):
   prefill_varlen / partitioned_varlen / decode_varlen
                                             ragged batches, packed [heads, rows, 128]
   decode_paged                              decode over a paged KV cache
-All of them give bitwise-identical rows for the same inputs and context.
+  prefill_lse / partitioned_lse / decode_lse
+                                            the same, also returning each row's log-sum-exp
+  backward(q, k, v, out, dout, lse)         deterministic dq, dk, dv of the causal prefill
+  attention(q, k, v)                        differentiable prefill (autograd glue)
+All forward entry points give bitwise-identical rows (and log-sum-exps) for
+the same inputs and context.
 """
 from __future__ import annotations
 
@@ -69,6 +74,18 @@ def lib() -> ctypes.CDLL:
         L.kb_attn_decode_paged.restype = ctypes.c_int
         L.kb_attn_decode_varlen_workspace_bytes.argtypes = [p64, i64, i32, i32]
         L.kb_attn_decode_varlen_workspace_bytes.restype = ctypes.c_size_t
+        L.kb_attn_prefill_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, vp]
+        L.kb_attn_prefill_lse.restype = ctypes.c_int
+        L.kb_attn_partitioned_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, f32, vp]
+        L.kb_attn_partitioned_lse.restype = ctypes.c_int
+        L.kb_attn_decode_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32, vp,
+                                         ctypes.c_size_t, vp]
+        L.kb_attn_decode_lse.restype = ctypes.c_int
+        L.kb_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, vp,
+                                       ctypes.c_size_t, vp]
+        L.kb_attn_backward.restype = ctypes.c_int
+        L.kb_attn_backward_workspace_bytes.argtypes = [i64, i64, i32, i32]
+        L.kb_attn_backward_workspace_bytes.restype = ctypes.c_size_t
         L.kb_attn_strerror.argtypes = [ctypes.c_int]
         L.kb_attn_strerror.restype = ctypes.c_char_p
         L.kb_attn_contract.argtypes = [ctypes.POINTER(i32)] * 3
@@ -284,6 +301,126 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float | None 
     return out
 
 
+def _lse_out(lse, shape, like):
+    torch = _torch()
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=like.device)
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda
+            or tuple(lse.shape) != tuple(shape) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 GPU tensor of shape {tuple(shape)}")
+    return lse
+
+
+def prefill_lse(q, k, v, scale: float | None = None, out=None, lse=None):
+    """prefill() that also returns the fp32 log-sum-exp of every row, [B, Hq, S]."""
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(n, x)
+    B, Hq, S, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    out = _torch().empty_like(q) if out is None else out
+    _check_tensor("out", out)
+    lse = _lse_out(lse, (B, Hq, S), q)
+    check(lib().kb_attn_prefill_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, S,
+                                    Hq, k.shape[1], D, _scale(scale, D), _stream(q)))
+    return out, lse
+
+
+def partitioned_lse(q, k_cache, v_cache, kv_len: int, scale: float | None = None, out=None, lse=None):
+    """partitioned() that also returns the fp32 log-sum-exp of every row, [B, Hq, q_len]."""
+    for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(n, x)
+    B, Hq, q_len, D = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shape mismatch")
+    out = _torch().empty_like(q) if out is None else out
+    _check_tensor("out", out)
+    lse = _lse_out(lse, (B, Hq, q_len), q)
+    check(lib().kb_attn_partitioned_lse(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), B, q_len, int(kv_len), k_cache.shape[2], Hq,
+                                        k_cache.shape[1], D, _scale(scale, D), _stream(q)))
+    return out, lse
+
+
+def decode_lse(q, k_cache, v_cache, kv_len: int | None = None, scale: float | None = None, out=None, lse=None,
+               workspace=None):
+    """decode() that also returns the fp32 log-sum-exp of every row, [B, Hq, 1]."""
+    torch = _torch()
+    for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(n, x)
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per sequence")
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shape mismatch")
+    kv_len = k_cache.shape[2] if kv_len is None else int(kv_len)
+    need = decode_workspace_bytes(B, kv_len, Hq, D) if kv_len >= 1 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out)
+    lse = _lse_out(lse, (B, Hq, 1), q)
+    check(lib().kb_attn_decode_lse(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, kv_len, k_cache.shape[2], Hq, k_cache.shape[1], D,
+                                   _scale(scale, D), ws_ptr, ws_bytes, _stream(q)))
+    return out, lse
+
+
+def backward_workspace_bytes(batch: int, seq_len: int, n_q_heads: int = 32, head_dim: int = HEAD_DIM) -> int:
+    return int(lib().kb_attn_backward_workspace_bytes(batch, seq_len, n_q_heads, head_dim))
+
+
+def backward(q, k, v, out, dout, lse, scale: float | None = None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of the causal full-sequence forward for the
+    upstream gradient dout, from the forward's out and lse (prefill_lse)."""
+    torch = _torch()
+    for n, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_tensor(n, x)
+    B, Hq, S, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must be shaped like q")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda
+            or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous()):
+        raise ValueError("lse must be the contiguous float32 [B, Hq, S] tensor of the forward")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(n, x)
+    need = backward_workspace_bytes(B, S, Hq, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib().kb_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, Hq, k.shape[1], D,
+                                 _scale(scale, D), workspace.data_ptr(), ws_bytes, _stream(q)))
+    return dq, dk, dv
+
+
+def attention(q, k, v, scale: float | None = None):
+    """Differentiable causal attention: forward through prefill_lse, backward
+    through backward (torch autograd glue only)."""
+    torch = _torch()
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q_, k_, v_):
+            o, lse = prefill_lse(q_, k_, v_, scale)
+            ctx.save_for_backward(q_, k_, v_, o, lse)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q_, k_, v_, o, lse = ctx.saved_tensors
+            return backward(q_, k_, v_, o, do.contiguous(), lse, scale)
+
+    return _Attention.apply(q, k, v)
+
+
 def unified_prefill(q, k, v, H_Q: int, H_KV: int, scale: float | None = None):
     """The README's call shape: causal forward, output shaped like q."""
     if q.shape[1] != H_Q or k.shape[1] != H_KV:
@@ -299,4 +436,6 @@ def unified_decode(q_last, k, v, H_Q: int, H_KV: int, scale: float | None = None
 
 
 __all__ = ["prefill", "partitioned", "decode", "unified_prefill", "unified_decode", "contract",
-           "decode_workspace_bytes", "lib", "check", "KBAttnError", "LIB_PATH"]
+           "decode_workspace_bytes", "prefill_varlen", "partitioned_varlen", "decode_varlen",
+           "decode_varlen_workspace_bytes", "decode_paged", "prefill_lse", "partitioned_lse", "decode_lse",
+           "backward", "backward_workspace_bytes", "attention", "lib", "check", "KBAttnError", "LIB_PATH"]

@@ -9,6 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkb_attn.so")
+# the forward (the bitwise contract's kernels) and the backward
+SOURCES = ["kb_attn.hip", "kb_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -32,9 +34,9 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     """Always recompiles libkb_attn.so; returns its path."""
-    src = os.path.join(CSRC, "kb_attn.hip")
+    srcs = [os.path.join(CSRC, name) for name in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), src, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -19,6 +19,8 @@
 #include <cmath>
 #include <algorithm>
 #include <cstdint>
+#include <initializer_list>
+#include <utility>
 #include <vector>
 
 #include "../../include/kb_attn.h"
@@ -33,6 +35,7 @@ struct PrefillArgs {
     const uint16_t* k;
     const uint16_t* v;
     uint16_t* o;
+    float* lse;  // optional: [batch, Hq, q_len] log-sum-exp of each row
     int64_t q_len, kv_len, cap;
     int32_t batch, n_kv_heads;
     int32_t pb_first, n_pb;  // 64-position blocks covered by the call
@@ -46,6 +49,7 @@ constexpr int kStages = 3;
 struct PrefillWork {
     const uint16_t* q0;  // row 0 of this (sequence, KV head group): query head 4g + i at q0 + i * q_hstride rows
     uint16_t* o0;        // same for the output
+    float* lse0;         // optional log-sum-exp output: head 4g + i, row r at lse0[i * q_hstride + r]
     int64_t q_hstride;   // rows between consecutive query heads
     const uint16_t* kbase;  // key 0 of this (sequence, KV head)
     const uint16_t* vbase;
@@ -173,6 +177,7 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
                 *reinterpret_cast<uint2*>(orow + 32 * db + 8 * b4 + 4 * h) = packed;
             }
         }
+        if (wk.lse0 && h == 0) wk.lse0[qrow0 + r] = lse_of(Mc, L);
     }
 }
 
@@ -200,6 +205,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
     PrefillWork wk;
     wk.q0 = a.q + ((int64_t)b * n_q_heads + kGroup * g) * a.q_len * kHeadDim;
     wk.o0 = a.o + ((int64_t)b * n_q_heads + kGroup * g) * a.q_len * kHeadDim;
+    wk.lse0 = a.lse ? a.lse + ((int64_t)b * n_q_heads + kGroup * g) * a.q_len : nullptr;
     wk.q_hstride = a.q_len;
     const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
     wk.kbase = a.k + kvoff;
@@ -247,6 +253,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_varlen_kernel(Varl
     PrefillWork wk;
     wk.q0 = a.q + ((int64_t)kGroup * g * a.q_rows + t.q_row0[s]) * kHeadDim;
     wk.o0 = a.o + ((int64_t)kGroup * g * a.q_rows + t.q_row0[s]) * kHeadDim;
+    wk.lse0 = nullptr;
     wk.q_hstride = a.q_rows;
     wk.kbase = a.k + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
     wk.vbase = a.v + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
@@ -263,6 +270,7 @@ struct DecodeArgs {
     uint16_t* o;
     float* ws_o;   // [batch * n_q_heads * n_chunks][128]
     float* ws_ml;  // [batch * n_q_heads * n_chunks][2]: (max * c, sum)
+    float* lse;    // optional: [batch, Hq] log-sum-exp of each row
     int64_t kv_len, cap;
     int32_t batch, n_kv_heads, n_chunks;
     float c;
@@ -289,6 +297,7 @@ __device__ __forceinline__ void wait_tiles_decode(int ahead) {
 struct DecodeWork {
     const uint16_t* q;  // query head 4g + i at row q_row0 + i * q_hstride
     uint16_t* o;        // output rows, same indexing
+    float* lse;         // optional log-sum-exp output, same row indexing
     int64_t q_row0, q_hstride;
     const uint16_t* kbase;  // key 0 of this (sequence, KV head)
     const uint16_t* vbase;
@@ -400,6 +409,7 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
             packed.y = e2 | (e3 << 16);
             *reinterpret_cast<uint2*>(orow + 32 * w + 8 * b4 + 4 * h) = packed;
         }
+        if (wk.lse && w == 0 && h == 0) wk.lse[qrow_idx] = lse_of(mc, l);
         return;
     }
     const int64_t prow = wk.ws_row0 + (int64_t)hi * wk.n_chunks + chunk;
@@ -430,6 +440,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     DecodeWork wk;
     wk.q = a.q;
     wk.o = a.o;
+    wk.lse = a.lse;
     wk.q_row0 = (int64_t)b * n_q_heads + kGroup * g;
     wk.q_hstride = 1;
     const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
@@ -446,14 +457,15 @@ struct CombineArgs {
     const float* ws_o;
     const float* ws_ml;
     uint16_t* o;
+    float* lse;  // optional: [rows] log-sum-exp
     int32_t n_chunks;
     float c;
 };
 
 // Fold the chunk partials of one output row in chunk order and finalize;
-// thread d owns output element d.
+// thread d owns output element d; thread 0 writes the log-sum-exp when asked.
 __device__ __forceinline__ void combine_row(const float* ws_o, const float* ws_ml, int64_t base, int n_chunks,
-                                            uint16_t* orow) {
+                                            uint16_t* orow, float* lse_row) {
     const int d = threadIdx.x;
     float Mc = ws_ml[base * 2 + 0];
     float L = ws_ml[base * 2 + 1];
@@ -469,13 +481,14 @@ __device__ __forceinline__ void combine_row(const float* ws_o, const float* ws_m
         Mc = Mcn;
     }
     orow[d] = finalize(O, L);
+    if (lse_row && d == 0) *lse_row = lse_of(Mc, L);
 }
 
 // One workgroup per (batch, query head): copy chunk 0, fold chunks 1.. in
 // order, finalize.
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     const int64_t row = blockIdx.x;
-    combine_row(a.ws_o, a.ws_ml, row * a.n_chunks, a.n_chunks, a.o + row * kHeadDim);
+    combine_row(a.ws_o, a.ws_ml, row * a.n_chunks, a.n_chunks, a.o + row * kHeadDim, a.lse ? a.lse + row : nullptr);
 }
 
 // Ragged decode: one query token per sequence, q, o [Hq, n_seq_total, 128]
@@ -520,6 +533,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_varlen_kernel(Decode
     DecodeWork wk;
     wk.q = a.q;
     wk.o = a.o;
+    wk.lse = nullptr;
     wk.q_row0 = (int64_t)t.seq[s] * a.tok_stride + (int64_t)kGroup * g * a.head_stride;
     wk.q_hstride = a.head_stride;
     if (kPaged) {
@@ -550,7 +564,7 @@ __global__ __launch_bounds__(128) void combine_varlen_kernel(DecodeVarlenArgs a,
     const int nc = (int)((kv_len + kChunk - 1) / kChunk);
     if (nc == 1) return;
     combine_row(a.ws_o, a.ws_ml, t.ws_row0[s] + (int64_t)head * nc, nc,
-                a.o + ((int64_t)t.seq[s] * a.tok_stride + (int64_t)head * a.head_stride) * kHeadDim);
+                a.o + ((int64_t)t.seq[s] * a.tok_stride + (int64_t)head * a.head_stride) * kHeadDim, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -604,13 +618,15 @@ int check_device(std::initializer_list<const void*> ptrs) {
 
 int64_t n_chunks_of(int64_t kv_len) { return (kv_len + kChunk - 1) / kChunk; }
 
-int launch_prefill(bool partitioned, const void* q, const void* k, const void* v, void* o, int64_t batch,
-                   int64_t q_len, int64_t kv_len, int64_t cap, int32_t n_kv_heads, float scale, hipStream_t stream) {
+int launch_prefill(bool partitioned, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t batch, int64_t q_len, int64_t kv_len, int64_t cap, int32_t n_kv_heads, float scale,
+                   hipStream_t stream) {
     PrefillArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
     a.v = (const uint16_t*)v;
     a.o = (uint16_t*)o;
+    a.lse = lse;
     a.q_len = q_len;
     a.kv_len = kv_len;
     a.cap = cap;
@@ -753,10 +769,21 @@ int launch_decode_tables(const DecodeVarlenArgs& a, const std::vector<RaggedSeq>
 
 using namespace kb;
 
-extern "C" {
+namespace {
 
-int kb_attn_prefill(const void* q, const void* k, const void* v, void* o, int64_t batch, int64_t seq_len,
-                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale, hipStream_t stream) {
+// An optional log-sum-exp output of n_rows floats: 4-byte aligned device
+// memory of the current device that overlaps none of the other buffers
+// (alignment and overlap are checked before any device query).
+int check_lse(const float* lse, size_t n_rows, std::initializer_list<std::pair<const void*, size_t>> others) {
+    if (!lse) return KB_ATTN_OK;
+    if ((uintptr_t)lse & 3u) return KB_ATTN_ERR_ALIGNMENT;
+    for (const auto& o : others)
+        if (ranges_overlap(lse, n_rows * sizeof(float), o.first, o.second)) return KB_ATTN_ERR_ALIAS;
+    return check_device({lse});
+}
+
+int prefill_entry(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch, int64_t seq_len,
+                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale, hipStream_t stream) {
     if (!q || !k || !v || !o || batch < 1 || seq_len < 1) return KB_ATTN_ERR_INVALID_ARG;
     if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
     if (int rc = check_scale(scale)) return rc;
@@ -767,13 +794,16 @@ int kb_attn_prefill(const void* q, const void* k, const void* v, void* o, int64_
     if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k, kvbytes) ||
         ranges_overlap(o, qbytes, v, kvbytes))
         return KB_ATTN_ERR_ALIAS;
+    if (int rc = check_lse(lse, (size_t)batch * n_q_heads * seq_len,
+                           {{q, qbytes}, {k, kvbytes}, {v, kvbytes}, {o, qbytes}}))
+        return rc;
     if (int rc = check_device({q, k, v, o})) return rc;
-    return launch_prefill(false, q, k, v, o, batch, seq_len, seq_len, seq_len, n_kv_heads, scale, stream);
+    return launch_prefill(false, q, k, v, o, lse, batch, seq_len, seq_len, seq_len, n_kv_heads, scale, stream);
 }
 
-int kb_attn_partitioned(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch,
-                        int64_t q_len, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
-                        int32_t head_dim, float scale, hipStream_t stream) {
+int partitioned_entry(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int64_t batch,
+                      int64_t q_len, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
+                      int32_t head_dim, float scale, hipStream_t stream) {
     if (!q || !k_cache || !v_cache || !o || batch < 1) return KB_ATTN_ERR_INVALID_ARG;
     if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
     if (int rc = check_scale(scale)) return rc;
@@ -785,21 +815,17 @@ int kb_attn_partitioned(const void* q, const void* k_cache, const void* v_cache,
     if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k_cache, kvbytes) ||
         ranges_overlap(o, qbytes, v_cache, kvbytes))
         return KB_ATTN_ERR_ALIAS;
+    if (int rc = check_lse(lse, (size_t)batch * n_q_heads * q_len,
+                           {{q, qbytes}, {k_cache, kvbytes}, {v_cache, kvbytes}, {o, qbytes}}))
+        return rc;
     if (int rc = check_device({q, k_cache, v_cache, o})) return rc;
-    return launch_prefill(true, q, k_cache, v_cache, o, batch, q_len, kv_len, kv_capacity, n_kv_heads, scale,
+    return launch_prefill(true, q, k_cache, v_cache, o, lse, batch, q_len, kv_len, kv_capacity, n_kv_heads, scale,
                           stream);
 }
 
-size_t kb_attn_decode_workspace_bytes(int64_t batch, int64_t kv_len, int32_t n_q_heads, int32_t head_dim) {
-    if (batch < 1 || kv_len < 1 || n_q_heads < 1 || head_dim != kHeadDim || kv_len > kMaxLen) return 0;
-    const int64_t nc = n_chunks_of(kv_len);
-    if (nc == 1) return 0;
-    return (size_t)batch * n_q_heads * nc * (kHeadDim + 2) * sizeof(float);
-}
-
-int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch, int64_t kv_len,
-                   int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
-                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int decode_entry(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int64_t batch,
+                 int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                 float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!q || !k_cache || !v_cache || !o || batch < 1) return KB_ATTN_ERR_INVALID_ARG;
     if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
     if (int rc = check_scale(scale)) return rc;
@@ -816,6 +842,10 @@ int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
     if (need && (ranges_overlap(workspace, need, q, qbytes) || ranges_overlap(workspace, need, k_cache, kvbytes) ||
                  ranges_overlap(workspace, need, v_cache, kvbytes)))
         return KB_ATTN_ERR_ALIAS;
+    if (int rc = check_lse(lse, (size_t)batch * n_q_heads,
+                           {{q, qbytes}, {k_cache, kvbytes}, {v_cache, kvbytes}, {o, qbytes},
+                            {need ? workspace : nullptr, need}}))
+        return rc;
     if (int rc = check_device({q, k_cache, v_cache, o, need ? workspace : nullptr})) return rc;
 
     const int64_t nc = n_chunks_of(kv_len);
@@ -827,6 +857,7 @@ int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
     a.o = (uint16_t*)o;
     a.ws_o = need ? (float*)workspace : nullptr;
     a.ws_ml = need ? (float*)workspace + rows * nc * kHeadDim : nullptr;
+    a.lse = lse;
     a.kv_len = kv_len;
     a.cap = kv_capacity;
     a.batch = (int32_t)batch;
@@ -842,12 +873,66 @@ int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
         cmb.ws_o = a.ws_o;
         cmb.ws_ml = a.ws_ml;
         cmb.o = a.o;
+        cmb.lse = lse;
         cmb.n_chunks = (int32_t)nc;
         cmb.c = a.c;
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(kHeadDim), 0, stream, cmb);
         if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
     }
     return KB_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kb_attn_prefill(const void* q, const void* k, const void* v, void* o, int64_t batch, int64_t seq_len,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale, hipStream_t stream) {
+    return prefill_entry(q, k, v, o, nullptr, batch, seq_len, n_q_heads, n_kv_heads, head_dim, scale, stream);
+}
+
+int kb_attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch,
+                        int64_t seq_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                        hipStream_t stream) {
+    if (!lse) return KB_ATTN_ERR_INVALID_ARG;
+    return prefill_entry(q, k, v, o, lse, batch, seq_len, n_q_heads, n_kv_heads, head_dim, scale, stream);
+}
+
+int kb_attn_partitioned(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch,
+                        int64_t q_len, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
+                        int32_t head_dim, float scale, hipStream_t stream) {
+    return partitioned_entry(q, k_cache, v_cache, o, nullptr, batch, q_len, kv_len, kv_capacity, n_q_heads,
+                             n_kv_heads, head_dim, scale, stream);
+}
+
+int kb_attn_partitioned_lse(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                            int64_t batch, int64_t q_len, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, float scale, hipStream_t stream) {
+    if (!lse) return KB_ATTN_ERR_INVALID_ARG;
+    return partitioned_entry(q, k_cache, v_cache, o, lse, batch, q_len, kv_len, kv_capacity, n_q_heads, n_kv_heads,
+                             head_dim, scale, stream);
+}
+
+size_t kb_attn_decode_workspace_bytes(int64_t batch, int64_t kv_len, int32_t n_q_heads, int32_t head_dim) {
+    if (batch < 1 || kv_len < 1 || n_q_heads < 1 || head_dim != kHeadDim || kv_len > kMaxLen) return 0;
+    const int64_t nc = n_chunks_of(kv_len);
+    if (nc == 1) return 0;
+    return (size_t)batch * n_q_heads * nc * (kHeadDim + 2) * sizeof(float);
+}
+
+int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch, int64_t kv_len,
+                   int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_entry(q, k_cache, v_cache, o, nullptr, batch, kv_len, kv_capacity, n_q_heads, n_kv_heads, head_dim,
+                        scale, workspace, workspace_bytes, stream);
+}
+
+int kb_attn_decode_lse(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int64_t batch,
+                       int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                       float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!lse) return KB_ATTN_ERR_INVALID_ARG;
+    return decode_entry(q, k_cache, v_cache, o, lse, batch, kv_len, kv_capacity, n_q_heads, n_kv_heads, head_dim,
+                        scale, workspace, workspace_bytes, stream);
 }
 
 int kb_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, const int64_t* cu_seqlens,

@@ -1,0 +1,567 @@
+// kb_bwd: deterministic backward of the causal GQA attention for gfx950.
+//
+// The pages cover the forward only (KernelBraid / AReaL-TIK README,
+// "Features": the release covers forward attention; "Background": training
+// forward and backward still run).  This is the gradient of that forward for
+// full causal sequences, recomputing P from the log-sum-exp the forward
+// returns (the usual flash-attention recomputation), with every output
+// element reduced in one fixed order -- no atomics -- so its bits depend only
+// on the inputs:
+//
+//   bwd_prep_kernel  D_i = <dO_i, O_i> and lse2_i = lse_i * log2(e) per row
+//   bwd_dkdv_kernel  one wave per 32 keys of a KV head; the Q / dO rows of
+//                    the 4 query heads stream through LDS in 32-row tiles:
+//                      S    = Q K^T           (A = Q rows,  B = K rows in registers)
+//                      dP   = dO V^T          (A = dO rows, B = V rows in registers)
+//                      P    = exp2(S c - lse2),  dS = P (dP - D)
+//                      dV^T += dO^T P,  dK^T += Q^T dS   (A read transposed from LDS)
+//   bwd_dq_kernel    one wave per 32 query rows; K / V tiles of 64 keys stream
+//                    through LDS as in the forward:
+//                      S^T  = K Q^T,  dP^T = V dO^T,  dQ^T += K^T dS^T
+// All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS
+// are rounded to bf16 (RNE) as the operands of the second products.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <initializer_list>
+
+#include "../../include/kb_attn.h"
+#include "kb_contract.h"
+
+namespace kb {
+namespace bwd {
+
+// ---------------------------------------------------------------------------
+// LDS tiles: rows of 256 bytes (128 bf16), 16-byte chunk c of row r stored at
+// chunk position c ^ swz(r).  Tiles read both by rows and transposed use
+//   dual(r) = ((r & 3) << 2) | ((r >> 2) & 3)
+// which gives 16 distinct positions for the row reads (16 consecutive rows,
+// one chunk) and for the transposing reads (4 consecutive rows x 4
+// consecutive chunks); tiles read only by rows use r & 15.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int dual_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+template <bool kDual>
+__device__ __forceinline__ int swz(int row) {
+    return kDual ? dual_swz(row) : (row & 15);
+}
+
+// Direct-to-LDS loads of rows row0 .. row0 + 4 * n_instr - 1 of a [rows, 128]
+// bf16 matrix into an LDS tile; rows beyond last_row read last_row (they are
+// masked or weighted by zero later).  This wave issues instructions
+// i = first, first + step, ... < n_instr; instruction i fills tile rows
+// 4i .. 4i + 3, lane L landing at tile byte 1024 i + 16 L.
+template <bool kDual>
+__device__ __forceinline__ void stage_rows(const uint16_t* base, int64_t row0, int64_t last_row, char* tile,
+                                           int first, int step, int n_instr, int lane) {
+    const char* tb = reinterpret_cast<const char*>(base + row0 * kHeadDim);
+    for (int i = first; i < n_instr; i += step) {
+        const int row = 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ swz<kDual>(row);
+        int64_t r = row0 + row;
+        r = r < last_row ? r : last_row;
+        const uint32_t voff = (uint32_t)((r - row0) * 256 + c * 16);
+        lds_dma16(tb, voff, tile + 1024 * i);
+    }
+}
+
+// Row fragment: lane (row 32 blk + (lane & 31), half h) holds bf16
+// [16 st + 8h, 16 st + 8h + 7] of its row -- the A operand of a product whose
+// rows are the tile's rows, or the B operand whose columns are.
+template <bool kDual>
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int blk, int st, int lane) {
+    const int row = 32 * blk + (lane & 31);
+    const int c = 2 * st + (lane >> 5);
+    return lds_read16(tile + row * 256 + ((c ^ swz<kDual>(row)) << 4));
+}
+
+// Transposed fragment (dual swizzle): the A operand X^T[d][rows] for d block
+// dblk and the 16-row step (blk, u) of the tile, with the row order of an
+// MFMA result column: lane (d = 32 dblk + j, half h) holds, in slot order,
+//   X[R0 + 4h + {0..3}][d], X[R0 + 8 + 4h + {0..3}][d],   R0 = 32 blk + 16 u
+// (two ds_read_b64_tr_b16; same addressing as the forward's V^T reads).
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int blk, int u, int dblk, int lane) {
+    const int g = lane >> 4, n = (lane >> 2) & 3, jj = lane & 3;
+    const int row0 = 32 * blk + 16 * u + 4 * (g >> 1) + n;
+    const int d = 32 * dblk + 16 * (g & 1) + 4 * jj;
+    const int c = d >> 3, half = (d & 4) << 1;
+    const int row1 = row0 + 8;
+    const char* p0 = tile + row0 * 256 + ((c ^ dual_swz(row0)) << 4) + half;
+    const char* p1 = tile + row1 * 256 + ((c ^ dual_swz(row1)) << 4) + half;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 all = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, all);
+}
+
+// bf16 (RNE) of elements 8u .. 8u + 7 of an MFMA result: the k-slots of the
+// 16-row step u in the order tr_frag reads the other operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int u) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        f32x2 pp;
+        pp[0] = x[8 * u + e];
+        pp[1] = x[8 * u + e + 1];
+        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+        r[e] = pb[0];
+        r[e + 1] = pb[1];
+    }
+    return r;
+}
+
+// Stores 16 fp32 of an MFMA result column, times `mul`, as bf16 into row
+// `dst` (128 elements): element v holds d = 32 dblk + 8 (v >> 2) + 4h + (v & 3).
+__device__ __forceinline__ void store_col(uint16_t* dst, const f32x16 (&acc)[4], float mul, int h) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+            uint32_t e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const __bf16 x = (__bf16)(acc[db][4 * b4 + i] * mul);
+                e[i] = __builtin_bit_cast(uint16_t, x);
+            }
+            uint2 packed;
+            packed.x = e[0] | (e[1] << 16);
+            packed.y = e[2] | (e[3] << 16);
+            *reinterpret_cast<uint2*>(dst + 32 * db + 8 * b4 + 4 * h) = packed;
+        }
+    }
+}
+
+constexpr float kLog2e = 1.44269502f;  // fp32(log2 e)
+
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* ws_d;     // [batch * Hq, s_pad]  D_i
+    float* ws_lse2;  // [batch * Hq, s_pad]  lse_i * log2 e
+    int64_t seq_len, s_pad;
+    int32_t batch, n_kv_heads;
+    float c;      // fp32(scale * log2 e), as in the forward
+    float scale;  // fp32 scale
+};
+
+// ---------------------------------------------------------------------------
+// D and lse2 per row: 8 lanes per row, 16 elements per lane in order, then a
+// fixed xor butterfly over the 8 lanes.  Rows i >= seq_len of the padded
+// arrays get 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int part = threadIdx.x & 7;
+    const int64_t n_rows = (int64_t)a.batch * kGroup * a.n_kv_heads * a.s_pad;
+    const bool in_range = row < n_rows;
+    const int64_t bh = in_range ? row / a.s_pad : 0;
+    const int64_t i = in_range ? row % a.s_pad : 0;
+    const bool valid = in_range && i < a.seq_len;
+    float acc = 0.0f;
+    if (valid) {
+        const int64_t src = (bh * a.seq_len + i) * kHeadDim + 16 * part;
+        const u32x4* dp = reinterpret_cast<const u32x4*>(a.dout + src);
+        const u32x4* op = reinterpret_cast<const u32x4*>(a.o + src);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const bf16x8 x = __builtin_bit_cast(bf16x8, dp[half]);
+            const bf16x8 y = __builtin_bit_cast(bf16x8, op[half]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+        }
+    }
+    acc = acc + __shfl_xor(acc, 1);
+    acc = acc + __shfl_xor(acc, 2);
+    acc = acc + __shfl_xor(acc, 4);
+    if (in_range && part == 0) {
+        a.ws_d[row] = valid ? acc : 0.0f;
+        a.ws_lse2[row] = valid ? a.lse[bh * a.seq_len + i] * kLog2e : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: workgroup = 4 waves on 128 keys [K0, K0 + 128) of one (sequence,
+// KV head); wave w owns keys K0 + 32 w .. + 31 and keeps their K and V rows
+// in registers.  Work items t = 0, 1, ...: query tile q0 = K0 + 32 (t / 4)
+// of query head 4g + (t % 4); each stage of the LDS ring holds the tile's
+// Q rows, dO rows (dual swizzle) and its 32 lse2 and 32 D values.  dK^T and
+// dV^T accumulate over the items in order.
+// ---------------------------------------------------------------------------
+constexpr int kKvWaves = 4;
+constexpr int kKvKeys = 32 * kKvWaves;
+constexpr int kQTileBytes = 32 * 256;
+constexpr int kKvStageBytes = 2 * kQTileBytes + 256;  // Q, dO, lse2[32], D[32]
+constexpr int kKvStages = 3;
+constexpr int kKvLoadsPerWave = (2 * kQTileBytes / 1024) / kKvWaves + 1;  // 4 tile loads + 1 scalar block
+
+__device__ __forceinline__ void kv_stage(const BwdArgs& a, int64_t bh0, int t, int64_t K0, char* stage, int w,
+                                         int lane) {
+    const int64_t q0 = K0 + 32 * (t >> 2);
+    const int64_t bh = bh0 + (t & 3);  // (sequence, query head) row block
+    const uint16_t* qb = a.q + bh * a.seq_len * kHeadDim;
+    const uint16_t* db = a.dout + bh * a.seq_len * kHeadDim;
+    // 16 instructions: 0..7 fill Q, 8..15 fill dO; wave w issues w, w + 4, ...
+    stage_rows<true>(qb, q0, a.seq_len - 1, stage, w, kKvWaves, 8, lane);
+    stage_rows<true>(db, q0, a.seq_len - 1, stage + kQTileBytes, w, kKvWaves, 8, lane);
+    // lse2 / D of the 32 rows: wave w moves 16 floats with lanes 0..3
+    // (w = 0, 1: lse2[16w ..], w = 2, 3: D[16(w-2) ..]); padded arrays, in bounds
+    const float* src = (w < 2 ? a.ws_lse2 : a.ws_d) + bh * a.s_pad + q0 + 16 * (w & 1);
+    if (lane < 4) lds_dma16(reinterpret_cast<const char*>(src), (uint32_t)(lane * 16), stage + 2 * kQTileBytes + 64 * w);
+}
+
+__global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, h = lane >> 5;
+
+    const int n_kb = (int)((a.seq_len + kKvKeys - 1) / kKvKeys);
+    const int nbg = a.batch * a.n_kv_heads;
+    const int x = blockIdx.x;
+    int bg, kb;
+    if ((nbg & 7) == 0) {
+        // XCD k (x % 8) takes the (b, g) pairs k, k + 8, ..., each pair's key
+        // blocks longest work first, so the blocks of one pair share the
+        // Q / dO stream in that XCD's L2
+        const int i = x >> 3;
+        bg = (i / n_kb) * 8 + (x & 7);
+        kb = i % n_kb;
+    } else {
+        bg = x % nbg;
+        kb = x / nbg;
+    }
+    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
+    const int64_t S = a.seq_len;
+    const int64_t K0 = (int64_t)kb * kKvKeys;
+    const int64_t k0 = K0 + 32 * w;  // this wave's first key
+    const int64_t bh0 = (int64_t)b * kGroup * a.n_kv_heads + kGroup * g;
+    const int n_items = 4 * (int)((S - K0 + 31) / 32);
+
+    if (n_items >= 1) kv_stage(a, bh0, 0, K0, smem, w, lane);
+    if (n_items >= 2) kv_stage(a, bh0, 1, K0, smem + kKvStageBytes, w, lane);
+
+    // K and V rows of this wave's keys as B operands: lane (key j, half h)
+    // holds row k0 + j, d = 16 st + 8h .. + 7 (rows beyond S read row S - 1)
+    bf16x8 kf[8], vf[8];
+    {
+        int64_t key = k0 + j;
+        key = key < S ? key : S - 1;
+        const int64_t kvrow = ((int64_t)bg * S + key) * kHeadDim;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            kf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.k + kvrow + 16 * st + 8 * h));
+            vf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.v + kvrow + 16 * st + 8 * h));
+        }
+    }
+
+    f32x16 dK[4], dV[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        dK[db] = zero16();
+        dV[db] = zero16();
+    }
+    const float c = a.c;
+
+    for (int t = 0; t < n_items; ++t) {
+        // wait for this wave's loads of item t (the register loads above and
+        // item t + 1's stage may still be in flight), publish, refill
+        if (t + 1 < n_items)
+            wait_vm<kKvLoadsPerWave>();
+        else
+            wait_vm<0>();
+        __syncthreads();
+        if (t + 2 < n_items) kv_stage(a, bh0, t + 2, K0, smem + ((t + 2) % kKvStages) * kKvStageBytes, w, lane);
+
+        const int64_t q0 = K0 + 32 * (t >> 2);
+        if (q0 < k0) continue;  // every key of this wave lies after every row of the tile
+        const char* stage = smem + (t % kKvStages) * kKvStageBytes;
+        const char* sQ = stage;
+        const char* sD = stage + kQTileBytes;
+        const float* sL = reinterpret_cast<const float*>(stage + 2 * kQTileBytes);
+
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            s = mfma(row_frag<true>(sQ, 0, st, lane), kf[st], s);
+            dp = mfma(row_frag<true>(sD, 0, st, lane), vf[st], dp);
+        }
+        // element v: query q0 + 8 (v >> 2) + 4h + (v & 3), key k0 + j
+        const bool edge = (q0 == k0) || (q0 + 32 > S);
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+            const float4 l2 = *reinterpret_cast<const float4*>(sL + 8 * b4 + 4 * h);
+            const float4 dd = *reinterpret_cast<const float4*>(sL + 32 + 8 * b4 + 4 * h);
+            const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+            const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int v = 4 * b4 + i;
+                float p = exp2_hw(__builtin_fmaf(s[v], c, -lv[i]));
+                if (edge) {
+                    const int64_t qq = q0 + 8 * b4 + 4 * h + i;
+                    p = (k0 + j <= qq && qq < S) ? p : 0.0f;
+                }
+                s[v] = p;
+                dp[v] = p * (dp[v] - dv4[i]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 pb = pack8(s, u);
+            const bf16x8 sb = pack8(dp, u);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                dV[db] = mfma(tr_frag(sD, 0, u, db, lane), pb, dV[db]);
+                dK[db] = mfma(tr_frag(sQ, 0, u, db, lane), sb, dK[db]);
+            }
+        }
+    }
+
+    if (k0 + j < S) {
+        const int64_t row = ((int64_t)bg * S + k0 + j) * kHeadDim;
+        store_col(a.dk + row, dK, a.scale, h);
+        store_col(a.dv + row, dV, 1.0f, h);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: workgroup = 8 waves = the 4 query heads of one KV head x 2 halves of
+// the 64 positions [64 pb, 64 pb + 64), as in the forward; K / V tiles of 64
+// keys (K dual-swizzled, V rows only) stream through a 3-stage ring, loads two
+// tiles ahead.  Wave column j is query row 64 pb + 32 (w >> 2) + j.
+// ---------------------------------------------------------------------------
+constexpr int kDqWaves = 8;
+constexpr int kDqStages = 3;
+constexpr int kDqLoadsPerWave = kTileLoads / kDqWaves;
+
+__device__ __forceinline__ void dq_stage(const uint16_t* kb, const uint16_t* vb, int64_t key0, int64_t last,
+                                         char* stage, int w, int lane) {
+    stage_rows<true>(kb, key0, last, stage, w, kDqWaves, 16, lane);
+    stage_rows<false>(vb, key0, last, stage + kKBytes, w, kDqWaves, 16, lane);
+}
+
+__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kTileBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, h = lane >> 5;
+
+    const int64_t S = a.seq_len;
+    const int n_pb = (int)((S + 63) / 64);
+    const int nbg = a.batch * a.n_kv_heads;
+    const int x = blockIdx.x;
+    int bg, pbr;
+    if ((nbg & 7) == 0) {
+        const int i = x >> 3;
+        bg = (i / n_pb) * 8 + (x & 7);
+        pbr = i % n_pb;
+    } else {
+        bg = x % nbg;
+        pbr = x / nbg;
+    }
+    const int pb = n_pb - 1 - pbr;  // longest rows first
+    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
+    const int64_t bh = (int64_t)b * kGroup * a.n_kv_heads + kGroup * g + (w & 3);
+    const int64_t pos = (int64_t)pb * 64 + 32 * (w >> 2) + j;
+    const bool active = pos < S;
+    const uint16_t* kbase = a.k + (int64_t)bg * S * kHeadDim;
+    const uint16_t* vbase = a.v + (int64_t)bg * S * kHeadDim;
+    const int t_last = pb;
+
+    dq_stage(kbase, vbase, 0, S - 1, smem, w, lane);
+    if (t_last >= 1) dq_stage(kbase, vbase, kTile, S - 1, smem + kTileBytes, w, lane);
+
+    // B operands of this wave's rows: Q and dO, lane (row j, half h) holds d = 16 st + 8h .. + 7
+    bf16x8 qf[8], df[8];
+    float lse2 = 0.0f, Di = 0.0f;
+    {
+        const int64_t r = active ? pos : S - 1;
+        const int64_t qrow = (bh * S + r) * kHeadDim;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const u32x4 x4 = *reinterpret_cast<const u32x4*>(a.q + qrow + 16 * st + 8 * h);
+            const u32x4 y4 = *reinterpret_cast<const u32x4*>(a.dout + qrow + 16 * st + 8 * h);
+            qf[st] = __builtin_bit_cast(bf16x8, active ? x4 : zero);
+            df[st] = __builtin_bit_cast(bf16x8, active ? y4 : zero);
+        }
+        if (active) {
+            lse2 = a.ws_lse2[bh * a.s_pad + pos];
+            Di = a.ws_d[bh * a.s_pad + pos];
+        }
+    }
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = zero16();
+    const float c = a.c;
+
+    for (int t = 0; t <= t_last; ++t) {
+        if (t + 1 <= t_last)
+            wait_vm<kDqLoadsPerWave>();
+        else
+            wait_vm<0>();
+        __syncthreads();
+        if (t + 2 <= t_last) {
+            char* nb = smem + ((t + 2) % kDqStages) * kTileBytes;
+            dq_stage(kbase, vbase, (int64_t)(t + 2) * kTile, S - 1, nb, w, lane);
+        }
+        const char* sK = smem + (t % kDqStages) * kTileBytes;
+        const char* sV = sK + kKBytes;
+        const int64_t key0 = (int64_t)t * kTile;
+
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = zero16();
+            dp[kb] = zero16();
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                s[kb] = mfma(row_frag<true>(sK, kb, st, lane), qf[st], s[kb]);
+                dp[kb] = mfma(row_frag<false>(sV, kb, st, lane), df[st], dp[kb]);
+            }
+        }
+        // element v of block kb: key key0 + 32 kb + 8 (v >> 2) + 4h + (v & 3), row pos
+        const bool diag = t == t_last;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float p = exp2_hw(__builtin_fmaf(s[kb][v], c, -lse2));
+                if (diag) {
+                    const int64_t key = key0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+                    p = key <= pos ? p : 0.0f;
+                }
+                dp[kb][v] = p * (dp[kb][v] - Di);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16x8 sb = pack8(dp[kb], u);
+#pragma unroll
+                for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sK, kb, u, db, lane), sb, acc[db]);
+            }
+        }
+    }
+
+    if (active) store_col(a.dq + (bh * S + pos) * kHeadDim, acc, a.scale, h);
+}
+
+}  // namespace bwd
+}  // namespace kb
+
+using namespace kb;
+using namespace kb::bwd;
+
+namespace {
+
+constexpr int64_t kMaxSeq = int64_t(1) << 30;
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b || !an || !bn) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int on_device(std::initializer_list<const void*> ptrs) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return KB_ATTN_ERR_DEVICE;
+    }
+    for (const void* p : ptrs) {
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+            (void)hipGetLastError();
+            return KB_ATTN_ERR_DEVICE;
+        }
+        if (attr.type != hipMemoryTypeDevice || attr.device != dev) return KB_ATTN_ERR_DEVICE;
+    }
+    return KB_ATTN_OK;
+}
+
+int64_t padded_rows(int64_t seq_len) { return (seq_len + 63) / 64 * 64; }
+
+}  // namespace
+
+extern "C" {
+
+size_t kb_attn_backward_workspace_bytes(int64_t batch, int64_t seq_len, int32_t n_q_heads, int32_t head_dim) {
+    if (batch < 1 || seq_len < 1 || seq_len > kMaxSeq || n_q_heads < 1 || head_dim != kHeadDim) return 0;
+    return (size_t)2 * batch * n_q_heads * padded_rows(seq_len) * sizeof(float);
+}
+
+int kb_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int64_t batch, int64_t seq_len, int32_t n_q_heads,
+                     int32_t n_kv_heads, int32_t head_dim, float scale, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || batch < 1 || seq_len < 1)
+        return KB_ATTN_ERR_INVALID_ARG;
+    if (n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return KB_ATTN_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim || n_q_heads != kGroup * n_kv_heads) return KB_ATTN_ERR_UNSUPPORTED;
+    if (!(scale > 0.0f) || !(scale < __builtin_inff())) return KB_ATTN_ERR_INVALID_ARG;
+    if (seq_len > kMaxSeq || batch * n_kv_heads > INT32_MAX) return KB_ATTN_ERR_LENGTH;
+    const size_t need = kb_attn_backward_workspace_bytes(batch, seq_len, n_q_heads, head_dim);
+    if (!workspace || workspace_bytes < need) return KB_ATTN_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv, (const void*)workspace})
+        if ((uintptr_t)p & 15u) return KB_ATTN_ERR_ALIGNMENT;
+    if ((uintptr_t)lse & 3u) return KB_ATTN_ERR_ALIGNMENT;
+
+    const size_t qb = (size_t)batch * n_q_heads * seq_len * kHeadDim * 2;
+    const size_t kb_ = (size_t)batch * n_kv_heads * seq_len * kHeadDim * 2;
+    const size_t lb = (size_t)batch * n_q_heads * seq_len * sizeof(float);
+    const std::pair<const void*, size_t> outs[] = {{dq, qb}, {dk, kb_}, {dv, kb_}, {workspace, need}};
+    const std::pair<const void*, size_t> ins[] = {{q, qb}, {k, kb_}, {v, kb_}, {o, qb}, {dout, qb}, {lse, lb}};
+    for (size_t i = 0; i < 4; ++i) {
+        for (size_t m = i + 1; m < 4; ++m)
+            if (overlap(outs[i].first, outs[i].second, outs[m].first, outs[m].second)) return KB_ATTN_ERR_ALIAS;
+        for (const auto& in : ins)
+            if (overlap(outs[i].first, outs[i].second, in.first, in.second)) return KB_ATTN_ERR_ALIAS;
+    }
+    if (int rc = on_device({q, k, v, o, dout, lse, dq, dk, dv, workspace})) return rc;
+
+    BwdArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.o = (const uint16_t*)o;
+    a.dout = (const uint16_t*)dout;
+    a.lse = lse;
+    a.dq = (uint16_t*)dq;
+    a.dk = (uint16_t*)dk;
+    a.dv = (uint16_t*)dv;
+    a.seq_len = seq_len;
+    a.s_pad = padded_rows(seq_len);
+    a.ws_d = (float*)workspace;
+    a.ws_lse2 = (float*)workspace + (int64_t)batch * n_q_heads * a.s_pad;
+    a.batch = (int32_t)batch;
+    a.n_kv_heads = n_kv_heads;
+    a.c = (float)((double)scale * 1.4426950408889634073599246810019);
+    a.scale = scale;
+
+    const int64_t prep_rows = (int64_t)batch * n_q_heads * a.s_pad;
+    const int64_t prep_grid = (prep_rows + 31) / 32;
+    const int64_t nbg = batch * n_kv_heads;
+    const int64_t kv_grid = nbg * ((seq_len + kKvKeys - 1) / kKvKeys);
+    const int64_t dq_grid = nbg * ((seq_len + 63) / 64);
+    if (prep_grid > INT32_MAX || kv_grid > INT32_MAX || dq_grid > INT32_MAX) return KB_ATTN_ERR_LENGTH;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)prep_grid), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kv_grid), dim3(64 * kKvWaves), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)dq_grid), dim3(64 * kDqWaves), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+    return KB_ATTN_OK;
+}
+
+}  // extern "C"

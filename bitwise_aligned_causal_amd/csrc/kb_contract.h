@@ -29,6 +29,8 @@
 //     Mc' = max(Mc, mc); A = (Mc' == Mc) ? 1 : exp2(Mc - Mc')
 //     B   = (Mc' == mc) ? 1 : exp2(mc - Mc'); L = fma(L, A, l B); O = fma(O, A, o B)
 //   out = bf16_rne(O / L)  (IEEE division)
+//   lse = (Mc + log2(L)) * fp32(ln 2)   (v_log_f32; natural-log log-sum-exp
+//         of the scaled scores, emitted on request from the same (Mc, L))
 //
 // Compile every kernel of the library in one translation unit with
 // -ffp-contract=off so that no multiply-add is fused behind the contract's back.
@@ -500,6 +502,14 @@ __device__ __forceinline__ float fold_value(float O, float A, float o, float B) 
 __device__ __forceinline__ uint16_t finalize(float O, float L) {
     const __bf16 r = (__bf16)(O / L);
     return __builtin_bit_cast(uint16_t, r);
+}
+
+// Natural-log log-sum-exp of a row from its final (Mc, L): Mc + log2(L) is
+// log2 of sum_j 2^(c s_j) = log2 of sum_j exp(scale s_j).  L >= 1 (the key
+// that set the reference max contributes 2^0 or more), so v_log_f32 sees no
+// denormal.
+__device__ __forceinline__ float lse_of(float Mc, float L) {
+    return (Mc + __builtin_amdgcn_logf(L)) * 0.693147182f;
 }
 
 }  // namespace kb

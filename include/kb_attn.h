@@ -1,6 +1,7 @@
 /*
- * kb_attn -- bitwise-aligned causal grouped-query attention forward for
- * AMD Instinct MI355X (gfx950).
+ * kb_attn -- bitwise-aligned causal grouped-query attention for AMD
+ * Instinct MI355X (gfx950): the forward entry points, and a deterministic
+ * backward.
  *
  * The operator is the unified attention of the KernelBraid / AReaL-TIK README:
  *   - "Features": BF16, causal, contiguous [batch, heads, sequence, head_dim]
@@ -181,6 +182,62 @@ int kb_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages
                          int64_t batch, int64_t n_pages, int32_t page_size, int32_t n_q_heads,
                          int32_t n_kv_heads, int32_t head_dim, float scale, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The three dense entry points with a log-sum-exp output, for a backward
+ * pass (README "Background": training forward and backward still run beside
+ * the rollout; the pages define no backward, so this one is an extension).
+ * Arguments and outputs as in the plain call, plus
+ *   lse  fp32 [batch, n_q_heads, rows] (rows = seq_len, q_len or 1; DEVICE,
+ *        4-byte aligned, overlapping no other buffer, else
+ *        KB_ATTN_ERR_ALIGNMENT / KB_ATTN_ERR_ALIAS; NULL is
+ *        KB_ATTN_ERR_INVALID_ARG): log(sum_j exp(scale <q, k_j>)) over the
+ *        row's visible keys, computed from the contract's final fp32 state
+ *        (Mc, L) as (Mc + log2 L) * ln 2.
+ * The output bits o are those of the plain call, and the lse of a row is, like
+ * o, bit for bit the same from all three entry points.
+ */
+int kb_attn_prefill_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t batch, int64_t seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                        int32_t head_dim, float scale, hipStream_t stream);
+int kb_attn_partitioned_lse(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            float* lse, int64_t batch, int64_t q_len, int64_t kv_len,
+                            int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, float scale, hipStream_t stream);
+int kb_attn_decode_lse(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                       int64_t batch, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, float scale, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward of the causal full-sequence forward (an extension: the pages
+ * cover the forward only, README "Features" and "Background").  For the
+ * upstream gradient dout of o = attention(q, k, v):
+ *   dv_j = sum_i P_ij dout_i,   dS_ij = P_ij (<dout_i, v_j> - D_i),
+ *   D_i  = <dout_i, o_i>,  dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i
+ * with P_ij = exp(scale <q_i, k_j> - lse_i) recomputed in fp32 from the lse
+ * a *_lse forward returned, P and dS rounded to bf16 for the products (fp32
+ * accumulation), and dk, dv summed over the 4 query heads of each KV head.
+ * No atomics: every output element is reduced in one fixed order, so the
+ * result bits depend only on the inputs (not on the batch they share, the
+ * launch or the run).
+ *   q, o, dout, dq  [batch, n_q_heads, seq_len, 128] bf16 (DEVICE, 16-byte aligned)
+ *   k, v, dk, dv    [batch, n_kv_heads, seq_len, 128] bf16
+ *   lse             fp32 [batch, n_q_heads, seq_len] (DEVICE, 4-byte aligned)
+ *   workspace       DEVICE, 16-byte aligned, at least
+ *                   kb_attn_backward_workspace_bytes(...) bytes (per-row D_i
+ *                   and lse in log2 units); concurrent calls need separate ones
+ * dq, dk, dv must not overlap each other, any input or the workspace
+ * (KB_ATTN_ERR_ALIAS).  Other errors as for kb_attn_prefill.
+ */
+int kb_attn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int64_t batch, int64_t seq_len,
+                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes kb_attn_backward needs (0 for invalid sizes). */
+size_t kb_attn_backward_workspace_bytes(int64_t batch, int64_t seq_len, int32_t n_q_heads,
+                                        int32_t head_dim);
 
 /* Static description of an error code (never NULL). */
 const char* kb_attn_strerror(int code);

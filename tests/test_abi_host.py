@@ -124,3 +124,81 @@ def test_python_binding_refuses_cpu_tensors():
         kb.prefill(q, k, k)
     with pytest.raises(ValueError):
         kb.decode(q[:, :, :1].contiguous(), k, k)
+
+
+# ---- log-sum-exp entry points and the backward --------------------------------
+L = ctypes.c_void_p(0x10_0000_0000 + 5 * 0x1_0000_0000)
+
+
+def prefill_lse(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, batch=1, seq=16, hq=32, hkv=8, d=128, scale=SCALE)
+    a.update(kw)
+    return kb.lib().kb_attn_prefill_lse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["seq"], a["hq"],
+                                        a["hkv"], a["d"], a["scale"], None)
+
+
+def partitioned_lse(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, batch=1, q_len=8, kv_len=16, cap=16, hq=32, hkv=8, d=128, scale=SCALE)
+    a.update(kw)
+    return kb.lib().kb_attn_partitioned_lse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["q_len"],
+                                            a["kv_len"], a["cap"], a["hq"], a["hkv"], a["d"], a["scale"], None)
+
+
+def decode_lse(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, batch=1, kv_len=2048, cap=4096, hq=32, hkv=8, d=128, scale=SCALE, ws=W,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    return kb.lib().kb_attn_decode_lse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["kv_len"], a["cap"],
+                                       a["hq"], a["hkv"], a["d"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("call", [prefill_lse, partitioned_lse, decode_lse])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(lse=None), INVALID), (dict(q=None), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(lse=ctypes.c_void_p(L.value + 2)), ALIGN),
+    (dict(lse=Q), ALIAS), (dict(lse=ctypes.c_void_p(O.value + 4)), ALIAS), (dict(lse=K), ALIAS),
+])
+def test_lse_rejected_before_launch(call, kw, expect):
+    assert call(**kw) == expect
+
+
+def test_decode_lse_must_not_overlap_workspace():
+    assert decode_lse(lse=ctypes.c_void_p(W.value + 64)) == ALIAS
+
+
+DQ, DK, DV, DO = (ctypes.c_void_p(0x20_0000_0000 + i * 0x1_0000_0000) for i in range(4))
+
+
+def backward(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, batch=2, seq=300, hq=32, hkv=8, d=128,
+             scale=SCALE, ws=W, ws_bytes=1 << 20)
+    a.update(kw)
+    return kb.lib().kb_attn_backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                     a["batch"], a["seq"], a["hq"], a["hkv"], a["d"], a["scale"], a["ws"],
+                                     a["ws_bytes"], None)
+
+
+def test_backward_workspace_bytes():
+    # D and lse2 per row, rows padded to a multiple of 64
+    assert kb.backward_workspace_bytes(2, 300) == 2 * 2 * 32 * 320 * 4
+    assert kb.backward_workspace_bytes(1, 64) == 2 * 32 * 64 * 4
+    assert kb.backward_workspace_bytes(0, 64) == 0
+    assert kb.backward_workspace_bytes(1, 0) == 0
+    assert kb.lib().kb_attn_backward_workspace_bytes(1, 64, 32, 64) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(lse=None), INVALID), (dict(dq=None), INVALID),
+    (dict(dk=None), INVALID), (dict(dv=None), INVALID), (dict(o=None), INVALID),
+    (dict(batch=0), INVALID), (dict(seq=0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(hq=16), UNSUPPORTED), (dict(seq=(1 << 30) + 1), LENGTH),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=2 * 2 * 32 * 320 * 4 - 1), WORKSPACE),
+    (dict(dq=ctypes.c_void_p(DQ.value + 8)), ALIGN), (dict(lse=ctypes.c_void_p(L.value + 2)), ALIGN),
+    (dict(ws=ctypes.c_void_p(W.value + 4)), ALIGN),
+    (dict(dq=Q), ALIAS), (dict(dk=V), ALIAS), (dict(dv=DK), ALIAS), (dict(dq=DO), ALIAS),
+    (dict(dk=ctypes.c_void_p(L.value + 16)), ALIAS), (dict(ws=ctypes.c_void_p(DV.value + 4096)), ALIAS),
+    (dict(dv=O), ALIAS),
+])
+def test_backward_rejected_before_launch(kw, expect):
+    assert backward(**kw) == expect

@@ -1,0 +1,225 @@
+"""GPU parity of the log-sum-exp outputs and of the backward (through the C-ABI).
+
+Log-sum-exp: the library computes it from the contract's final fp32 state as
+(Mc + log2 L) ln 2, where L sums bf16-rounded terms; each term carries a
+relative rounding of at most 2^-9, so |lse - exact| <= 2^-9 + fp32 rounding.
+The test allows 2^-8 + 2^-20 |lse|.
+
+Gradients: the oracle returns, per element, the sum of the absolute values of
+the terms (its error budget e, see oracle/oracle.c).  The HIP path rounds P
+and dS to bf16 (2^-9 relative each), normalises P with a row sum of
+bf16-rounded terms (2^-9), computes D_i from the bf16 forward output
+(2^-9 of the output, plus the output's own error) and rounds the result to
+bf16 (2^-9 relative); fp32 accumulation adds far less.  Every term's relative
+error is below 2^-7, so |got - exact| <= 2^-7 e + 2^-8 |exact| element by
+element.  Those roundings have random signs, so the typical error is far
+smaller (measured: mean error 0.3-2% of the mean bound, rms error 0.25% of
+the rms gradient); the test also holds the mean error to a tenth of the mean
+bound and the rms error to 2^-7 of the rms gradient.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import kb_gen
+import oracle
+from gpu_util import bits, dev, note, oracle_threads
+
+pytestmark = pytest.mark.gpu
+
+HQ, HKV, D = 32, 8, 128
+SCALE = 1.0 / math.sqrt(D)
+
+
+def kb():
+    import bitwise_aligned_causal_amd as m
+
+    return m
+
+
+def f32(x):
+    return kb_gen.bf16_bits_to_f32(x).astype(np.float64)
+
+
+def make(seed, B, S):
+    q = kb_gen.normal_bf16(seed, 1, (B, HQ, S, D))
+    k = kb_gen.normal_bf16(seed, 2, (B, HKV, S, D))
+    v = kb_gen.normal_bf16(seed, 3, (B, HKV, S, D))
+    do = kb_gen.normal_bf16(seed, 4, (B, HQ, S, D))
+    return q, k, v, do
+
+
+def gpu_lse(t):
+    import torch
+
+    torch.cuda.synchronize()
+    return t.cpu().numpy().astype(np.float64)
+
+
+def check_lse(got, ref, what):
+    err = np.abs(got - ref)
+    tol = 2.0 ** -8 + 2.0 ** -20 * np.abs(ref)
+    worst = np.unravel_index(int((err - tol).argmax()), err.shape)
+    assert np.all(err <= tol), f"{what}: lse error {err[worst]:.3e} > {tol[worst]:.3e} at {worst}"
+
+
+def check_grad(got_bits, ref, budget, what):
+    got = kb_gen.bf16_bits_to_f32(got_bits).astype(np.float64).reshape(ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite gradient"
+    err = np.abs(got - ref)
+    bound = 2.0 ** -7 * budget + 2.0 ** -8 * np.abs(ref) + 1e-30
+    ratio = err / bound
+    worst = np.unravel_index(int(ratio.argmax()), ratio.shape)
+    assert ratio.max() <= 1.0, (f"{what}: error {err[worst]:.3e} at {worst} exceeds {bound[worst]:.3e} "
+                                f"(ref {ref[worst]:.3e}, budget {budget[worst]:.3e})")
+    # typical errors are random-signed roundings, far below the worst case:
+    # mean error within a tenth of the mean bound, rms error within 2^-7 of the rms gradient
+    assert err.mean() <= 0.1 * bound.mean(), f"{what}: mean error {err.mean():.3e} vs bound {bound.mean():.3e}"
+    rms_ref = math.sqrt(float((ref ** 2).mean()))
+    if rms_ref > 0:
+        assert math.sqrt(float((err ** 2).mean())) <= 2.0 ** -7 * rms_ref, f"{what}: rms error too large"
+    return float(ratio.max())
+
+
+def run_backward(q, k, v, do, seed_note=""):
+    m = kb()
+    Q, K, V, DO = dev(q), dev(k), dev(v), dev(do)
+    note(f"prefill_lse + backward B={q.shape[0]} S={q.shape[2]} {seed_note}")
+    o, lse = m.prefill_lse(Q, K, V)
+    dq, dk, dv = m.backward(Q, K, V, o, DO, lse)
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("B,S", [(1, 1), (1, 17), (2, 64), (1, 100), (1, 257), (2, 300), (1, 1024)])
+def test_backward_matches_oracle(B, S):
+    q, k, v, do = make(1000 + S, B, S)
+    _, lse, dq, dk, dv = run_backward(q, k, v, do)
+    check_lse(gpu_lse(lse), oracle.lse(q, k, v, threads=oracle_threads()), f"lse S={S}")
+    ref = oracle.backward(q, k, v, do, budgets=True, threads=oracle_threads())
+    check_grad(bits(dq), ref["dq"], ref["eq"], f"dq B={B} S={S}")
+    check_grad(bits(dk), ref["dk"], ref["ek"], f"dk B={B} S={S}")
+    check_grad(bits(dv), ref["dv"], ref["ev"], f"dv B={B} S={S}")
+
+
+def test_backward_outlier_inputs():
+    # strong outlier channels in q and k (score spread of tens of log2 units)
+    B, S = 1, 200
+    q, k, v, do = make(77, B, S)
+    qf, kf = kb_gen.bf16_bits_to_f32(q), kb_gen.bf16_bits_to_f32(k)
+    qf[..., :4] *= 8.0
+    kf[..., :4] *= 8.0
+    q, k = kb_gen.f32_to_bf16_bits(qf), kb_gen.f32_to_bf16_bits(kf)
+    _, lse, dq, dk, dv = run_backward(q, k, v, do, "outliers")
+    check_lse(gpu_lse(lse), oracle.lse(q, k, v, threads=oracle_threads()), "lse outliers")
+    ref = oracle.backward(q, k, v, do, budgets=True, threads=oracle_threads())
+    check_grad(bits(dq), ref["dq"], ref["eq"], "dq outliers")
+    check_grad(bits(dk), ref["dk"], ref["ek"], "dk outliers")
+    check_grad(bits(dv), ref["dv"], ref["ev"], "dv outliers")
+
+
+def test_backward_deterministic_and_batch_invariant():
+    import torch
+
+    m = kb()
+    B, S = 3, 333
+    q, k, v, do = make(5, B, S)
+    o, lse, dq, dk, dv = run_backward(q, k, v, do)
+    first = [bits(x) for x in (dq, dk, dv)]
+    Q, K, V, DO = dev(q), dev(k), dev(v), dev(do)
+    note("backward again, same inputs")
+    again = [bits(x) for x in m.backward(Q, K, V, o, DO, lse)]
+    for a, b in zip(first, again):
+        assert np.array_equal(a, b)
+    for i in range(B):
+        note(f"backward of sequence {i} alone")
+        sl = lambda x: np.ascontiguousarray(x[i:i + 1])
+        qi, ki, vi, doi = dev(sl(q)), dev(sl(k)), dev(sl(v)), dev(sl(do))
+        oi, lsei = m.prefill_lse(qi, ki, vi)
+        assert np.array_equal(bits(oi), bits(o)[i:i + 1])
+        assert torch.equal(lsei.cpu(), lse[i:i + 1].cpu())
+        one = [bits(x) for x in m.backward(qi, ki, vi, oi, doi, lsei)]
+        for name, a, b in zip(("dq", "dk", "dv"), one, first):
+            assert np.array_equal(a, b[i:i + 1]), f"{name} of sequence {i} depends on the batch"
+
+
+def test_lse_bitwise_across_entry_points():
+    import torch
+
+    m = kb()
+    B, S = 2, 2500
+    q, k, v, _ = make(11, B, S)
+    Q, K, V = dev(q), dev(k), dev(v)
+    note("prefill_lse vs prefill")
+    o, lse = m.prefill_lse(Q, K, V)
+    assert np.array_equal(bits(o), bits(m.prefill(Q, K, V)))
+    lse_np = lse.cpu().numpy()
+    # partitioned chunks that cross tile and chunk boundaries
+    start = 0
+    for n in (1, 63, 700, 1024, 712):
+        stop = start + n
+        note(f"partitioned_lse rows {start}..{stop}")
+        qc = dev(np.ascontiguousarray(q[:, :, start:stop]))
+        oc, lc = m.partitioned_lse(qc, K, V, stop)
+        assert np.array_equal(bits(oc), bits(o)[:, :, start:stop])
+        assert np.array_equal(lc.cpu().numpy().view(np.uint32), lse_np[:, :, start:stop].view(np.uint32))
+        start = stop
+    assert start == S
+    # decode of the last token at several contexts (one chunk and several)
+    for ctx in (1, 64, 1024, 1025, 2500):
+        note(f"decode_lse at context {ctx}")
+        qd = dev(np.ascontiguousarray(q[:, :, ctx - 1:ctx]))
+        od, ld = m.decode_lse(qd, K, V, ctx)
+        assert np.array_equal(bits(od)[:, :, 0], bits(o)[:, :, ctx - 1])
+        assert np.array_equal(ld.cpu().numpy()[:, :, 0].view(np.uint32), lse_np[:, :, ctx - 1].view(np.uint32))
+    torch.cuda.synchronize()
+
+
+def test_autograd_glue_matches_explicit_calls():
+    import torch
+
+    m = kb()
+    B, S = 1, 130
+    q, k, v, do = make(13, B, S)
+    Q, K, V, DO = (dev(x).requires_grad_(i < 3) for i, x in enumerate((q, k, v, do)))
+    note("autograd attention")
+    out = m.attention(Q, K, V)
+    out.backward(DO)
+    o, lse = m.prefill_lse(Q.detach(), K.detach(), V.detach())
+    dq, dk, dv = m.backward(Q.detach(), K.detach(), V.detach(), o, DO, lse)
+    assert np.array_equal(bits(out.detach()), bits(o))
+    for g, e in ((Q.grad, dq), (K.grad, dk), (V.grad, dv)):
+        assert np.array_equal(bits(g), bits(e))
+
+
+def test_backward_full_size_sampled():
+    """B=4, S=16384 (the training-shaped size the bench times): dq on sampled
+    rows, dk / dv on the last 64 keys (which only the last rows see), and the
+    softmax identities on every key."""
+    B, S = 4, 16384
+    q, k, v, do = make(21, B, S)
+    _, lse, dq, dk, dv = run_backward(q, k, v, do, "full size")
+    dq_b, dk_b, dv_b, lse_h = bits(dq), bits(dk), bits(dv), gpu_lse(lse)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([
+        rng.integers(0, B * HQ * S, size=48),
+        np.array([0, S - 1, S, 2 * S + 1023, B * HQ * S - 1]),
+    ])).astype(np.int64)
+    ref, budget = oracle.backward_dq_rows(q, k, v, do, rows, budgets=True, threads=oracle_threads())
+    check_grad(dq_b.reshape(-1, D)[rows], ref, budget, "dq sampled rows")
+    lref = oracle.lse(q, k, v, rows=rows, threads=oracle_threads())
+    check_lse(lse_h.reshape(-1)[rows], lref, "lse sampled rows")
+    # keys S-64 .. S-1 of sequence 0, all KV heads
+    q0, k0, v0, do0 = (np.ascontiguousarray(x[:1]) for x in (q, k, v, do))
+    tail = oracle.backward(q0, k0, v0, do0, row_from=S - 64, budgets=True, threads=oracle_threads())
+    check_grad(dk_b[:1, :, S - 64:], tail["dk"][:, :, S - 64:], tail["ek"][:, :, S - 64:], "dk last 64 keys")
+    check_grad(dv_b[:1, :, S - 64:], tail["dv"][:, :, S - 64:], tail["ev"][:, :, S - 64:], "dv last 64 keys")
+    # identities over all keys: sum_j dK_j = 0 and sum_j dV_j = sum of the group's dO
+    dkf = kb_gen.bf16_bits_to_f32(dk_b).astype(np.float64)
+    dvf = kb_gen.bf16_bits_to_f32(dv_b).astype(np.float64)
+    sk, ak = dkf.sum(axis=2), np.abs(dkf).sum(axis=2)
+    assert np.all(np.abs(sk) <= 2.0 ** -6 * ak), "sum_j dK_j is not ~0"
+    sv = dvf.sum(axis=2)
+    dos = kb_gen.bf16_bits_to_f32(do).astype(np.float64).reshape(B, HKV, 4, S, D).sum(axis=(2, 3))
+    scale_v = np.abs(dvf).sum(axis=2)
+    assert np.all(np.abs(sv - dos) <= 2.0 ** -6 * scale_v), "sum_j dV_j differs from the summed dO"
