@@ -9,12 +9,14 @@
 // on the inputs:
 //
 //   bwd_prep_kernel  D_i = <dO_i, O_i> and lse2_i = lse_i * log2(e) per row
-//   bwd_dkdv_kernel  one wave per 32 keys of a KV head; the Q / dO rows of
+//   bwd_dkdv_kernel  two waves per 32 keys of a KV head; the Q / dO rows of
 //                    the 4 query heads stream through LDS in 32-row tiles:
 //                      S    = Q K^T           (A = Q rows,  B = K rows in registers)
+//                      P    = exp2(S c - lse2),  dV^T += dO^T P        (first wave)
 //                      dP   = dO V^T          (A = dO rows, B = V rows in registers)
-//                      P    = exp2(S c - lse2),  dS = P (dP - D)
-//                      dV^T += dO^T P,  dK^T += Q^T dS   (A read transposed from LDS)
+//                      dS   = P (dP - D),  dK^T += Q^T dS            (second wave)
+//                    (the second operands read transposed from LDS; P passes
+//                    from the first wave to the second through LDS)
 //   bwd_dq_kernel    one wave per 32 query rows; K / V tiles of 64 keys stream
 //                    through LDS as in the forward:
 //                      S^T  = K Q^T,  dP^T = V dO^T,  dQ^T += K^T dS^T
@@ -46,22 +48,22 @@ __device__ __forceinline__ int swz(int row) {
     return kDual ? dual_swz(row) : (row & 15);
 }
 
-// Direct-to-LDS loads of rows row0 .. row0 + 4 * n_instr - 1 of a [rows, 128]
-// bf16 matrix into an LDS tile; rows beyond last_row read last_row (they are
-// masked or weighted by zero later).  This wave issues instructions
-// i = first, first + step, ... < n_instr; instruction i fills tile rows
-// 4i .. 4i + 3, lane L landing at tile byte 1024 i + 16 L.
+// Direct-to-LDS loads of a tile of 64 rows row0 .. row0 + 63 of a [rows, 128]
+// bf16 matrix; rows beyond last_row read last_row (they are masked or
+// weighted by zero later).  Instruction i (0..15) fills tile rows 4i .. 4i + 3,
+// lane L landing at tile byte 1024 i + 16 L; the wave issues instructions
+// first, first + step, ... (a rolled loop: it keeps no per-instruction
+// addresses live across the caller's loop).
 template <bool kDual>
 __device__ __forceinline__ void stage_rows(const uint16_t* base, int64_t row0, int64_t last_row, char* tile,
-                                           int first, int step, int n_instr, int lane) {
+                                           int first, int step, int lane) {
     const char* tb = reinterpret_cast<const char*>(base + row0 * kHeadDim);
-    for (int i = first; i < n_instr; i += step) {
+    const int64_t last = last_row - row0;
+    for (int i = first; i < 16; i += step) {
         const int row = 4 * i + (lane >> 4);
         const int c = (lane & 15) ^ swz<kDual>(row);
-        int64_t r = row0 + row;
-        r = r < last_row ? r : last_row;
-        const uint32_t voff = (uint32_t)((r - row0) * 256 + c * 16);
-        lds_dma16(tb, voff, tile + 1024 * i);
+        const int64_t r = row < last ? row : last;
+        lds_dma16(tb, (uint32_t)(r * 256 + c * 16), tile + 1024 * i);
     }
 }
 
@@ -188,39 +190,54 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 4 waves on 128 keys [K0, K0 + 128) of one (sequence,
-// KV head); wave w owns keys K0 + 32 w .. + 31 and keeps their K and V rows
-// in registers.  Work items t = 0, 1, ...: query tile q0 = K0 + 32 (t / 4)
-// of query head 4g + (t % 4); each stage of the LDS ring holds the tile's
-// Q rows, dO rows (dual swizzle) and its 32 lse2 and 32 D values.  dK^T and
-// dV^T accumulate over the items in order.
+// dK, dV: workgroup = 8 waves on 128 keys [K0, K0 + 128) of one (sequence,
+// KV head).  Key group kg = w & 3 covers keys k0 = K0 + 32 kg .. + 31 and is
+// served by two waves:
+//   P-wave  (w < 4)   S = Q K^T, P = exp2(S c - lse2), P to LDS, dV^T += dO^T P
+//   dS-wave (w >= 4)  one item later: dP = dO V^T, P from LDS,
+//                     dS = P (dP - D), dK^T += Q^T dS
+// so each wave holds one accumulator set (64 registers) and one of K, V.
+// Work items t = 0, 1, ...: query tile q0 = K0 + 32 (t / 4) of query head
+// 4g + (t % 4).  A 4-stage LDS ring holds each item's Q rows, dO rows (dual
+// swizzle) and its 32 lse2 and 32 D values, loaded two items ahead; P goes
+// through a double buffer.  dK^T and dV^T accumulate over the items in order.
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 4;
-constexpr int kKvKeys = 32 * kKvWaves;
+constexpr int kKvWaves = 8;
+constexpr int kKvKeys = 128;
 constexpr int kQTileBytes = 32 * 256;
 constexpr int kKvStageBytes = 2 * kQTileBytes + 256;  // Q, dO, lse2[32], D[32]
-constexpr int kKvStages = 3;
-constexpr int kKvLoadsPerWave = (2 * kQTileBytes / 1024) / kKvWaves + 1;  // 4 tile loads + 1 scalar block
+constexpr int kKvStages = 4;
+constexpr int kPBufBytes = 4 * 4096;                  // fp32 P of the 4 key groups
+constexpr int kKvLoadsPerWave = (2 * kQTileBytes / 1024) / kKvWaves + 1;  // 2 tile loads + 1 block of 8 floats
 
 __device__ __forceinline__ void kv_stage(const BwdArgs& a, int64_t bh0, int t, int64_t K0, char* stage, int w,
                                          int lane) {
     const int64_t q0 = K0 + 32 * (t >> 2);
     const int64_t bh = bh0 + (t & 3);  // (sequence, query head) row block
-    const uint16_t* qb = a.q + bh * a.seq_len * kHeadDim;
-    const uint16_t* db = a.dout + bh * a.seq_len * kHeadDim;
-    // 16 instructions: 0..7 fill Q, 8..15 fill dO; wave w issues w, w + 4, ...
-    stage_rows<true>(qb, q0, a.seq_len - 1, stage, w, kKvWaves, 8, lane);
-    stage_rows<true>(db, q0, a.seq_len - 1, stage + kQTileBytes, w, kKvWaves, 8, lane);
-    // lse2 / D of the 32 rows: wave w moves 16 floats with lanes 0..3
-    // (w = 0, 1: lse2[16w ..], w = 2, 3: D[16(w-2) ..]); padded arrays, in bounds
-    const float* src = (w < 2 ? a.ws_lse2 : a.ws_d) + bh * a.s_pad + q0 + 16 * (w & 1);
-    if (lane < 4) lds_dma16(reinterpret_cast<const char*>(src), (uint32_t)(lane * 16), stage + 2 * kQTileBytes + 64 * w);
+    const char* qb = reinterpret_cast<const char*>(a.q + (bh * a.seq_len + q0) * kHeadDim);
+    const char* db = reinterpret_cast<const char*>(a.dout + (bh * a.seq_len + q0) * kHeadDim);
+    const int64_t last = a.seq_len - 1 - q0;  // last valid row, relative to q0
+    // instructions 0..7 fill Q rows 4i..4i+3, 8..15 fill dO; wave w issues w and w + 8
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = w + 8 * k;
+        const int row = 4 * (i & 7) + (lane >> 4);
+        const int c = (lane & 15) ^ dual_swz(row);
+        const int64_t r = row < last ? row : last;
+        lds_dma16(i < 8 ? qb : db, (uint32_t)(r * 256 + c * 16), stage + 1024 * i);
+    }
+    // lse2 / D of the 32 rows (padded arrays, in bounds): wave w moves 8
+    // floats with lanes 0..1 (w < 4: lse2[8w ..], else D[8(w-4) ..])
+    const float* src = (w < 4 ? a.ws_lse2 : a.ws_d) + bh * a.s_pad + q0 + 8 * (w & 3);
+    if (lane < 2) lds_dma16(reinterpret_cast<const char*>(src), (uint32_t)(lane * 16), stage + 2 * kQTileBytes + 32 * w);
 }
 
 __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + 2 * kPBufBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = w & 3;
+    const bool pwave = w < 4;
     const int j = lane & 31, h = lane >> 5;
 
     const int n_kb = (int)((a.seq_len + kKvKeys - 1) / kKvKeys);
@@ -241,38 +258,33 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
     const int64_t S = a.seq_len;
     const int64_t K0 = (int64_t)kb * kKvKeys;
-    const int64_t k0 = K0 + 32 * w;  // this wave's first key
+    const int64_t k0 = K0 + 32 * kg;  // this wave's first key
     const int64_t bh0 = (int64_t)b * kGroup * a.n_kv_heads + kGroup * g;
     const int n_items = 4 * (int)((S - K0 + 31) / 32);
+    char* pbuf = smem + kKvStages * kKvStageBytes;
 
-    if (n_items >= 1) kv_stage(a, bh0, 0, K0, smem, w, lane);
+    kv_stage(a, bh0, 0, K0, smem, w, lane);
     if (n_items >= 2) kv_stage(a, bh0, 1, K0, smem + kKvStageBytes, w, lane);
 
-    // K and V rows of this wave's keys as B operands: lane (key j, half h)
-    // holds row k0 + j, d = 16 st + 8h .. + 7 (rows beyond S read row S - 1)
-    bf16x8 kf[8], vf[8];
+    // this wave's K (P-wave) or V (dS-wave) rows as B operands: lane (key j,
+    // half h) holds row k0 + j, d = 16 st + 8h .. + 7 (rows beyond S read row S - 1)
+    bf16x8 kvf[8];
     {
         int64_t key = k0 + j;
         key = key < S ? key : S - 1;
-        const int64_t kvrow = ((int64_t)bg * S + key) * kHeadDim;
+        const uint16_t* src = (pwave ? a.k : a.v) + ((int64_t)bg * S + key) * kHeadDim;
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            kf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.k + kvrow + 16 * st + 8 * h));
-            vf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.v + kvrow + 16 * st + 8 * h));
-        }
+        for (int st = 0; st < 8; ++st)
+            kvf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * st + 8 * h));
     }
 
-    f32x16 dK[4], dV[4];
+    f32x16 acc[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        dK[db] = zero16();
-        dV[db] = zero16();
-    }
+    for (int db = 0; db < 4; ++db) acc[db] = zero16();
     const float c = a.c;
 
-    for (int t = 0; t < n_items; ++t) {
-        // wait for this wave's loads of item t (the register loads above and
-        // item t + 1's stage may still be in flight), publish, refill
+    for (int t = 0; t <= n_items; ++t) {
+        // publish item t's stage (the item t + 1 stage may still be loading), refill
         if (t + 1 < n_items)
             wait_vm<kKvLoadsPerWave>();
         else
@@ -280,55 +292,73 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
         __syncthreads();
         if (t + 2 < n_items) kv_stage(a, bh0, t + 2, K0, smem + ((t + 2) % kKvStages) * kKvStageBytes, w, lane);
 
-        const int64_t q0 = K0 + 32 * (t >> 2);
-        if (q0 < k0) continue;  // every key of this wave lies after every row of the tile
-        const char* stage = smem + (t % kKvStages) * kKvStageBytes;
+        // the P-wave works on item t, the dS-wave on item t - 1
+        const int it = pwave ? t : t - 1;
+        if (it < 0 || it >= n_items) continue;
+        const int64_t q0 = K0 + 32 * (it >> 2);
+        if (q0 < k0) continue;  // every key of this group lies after every row of the tile
+        const char* stage = smem + (it % kKvStages) * kKvStageBytes;
         const char* sQ = stage;
         const char* sD = stage + kQTileBytes;
         const float* sL = reinterpret_cast<const float*>(stage + 2 * kQTileBytes);
+        float4* pb4 = reinterpret_cast<float4*>(pbuf + (it & 1) * kPBufBytes + kg * 4096);
 
-        f32x16 s = zero16(), dp = zero16();
+        if (pwave) {
+            f32x16 s = zero16();
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            s = mfma(row_frag<true>(sQ, 0, st, lane), kf[st], s);
-            dp = mfma(row_frag<true>(sD, 0, st, lane), vf[st], dp);
-        }
-        // element v: query q0 + 8 (v >> 2) + 4h + (v & 3), key k0 + j
-        const bool edge = (q0 == k0) || (q0 + 32 > S);
+            for (int st = 0; st < 8; ++st) s = mfma(row_frag<true>(sQ, 0, st, lane), kvf[st], s);
+            // element v: query q0 + 8 (v >> 2) + 4h + (v & 3), key k0 + j; it
+            // counts when k0 + j <= query < S, i.e. lo <= 8 (v >> 2) + (v & 3) < hi
+            const bool edge = (q0 == k0) || (q0 + 32 > S);
+            const int lo = (int)(k0 - q0) + j - 4 * h;
+            const int hi = (int)(S - q0 < 64 ? S - q0 : 64) - 4 * h;
 #pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-            const float4 l2 = *reinterpret_cast<const float4*>(sL + 8 * b4 + 4 * h);
-            const float4 dd = *reinterpret_cast<const float4*>(sL + 32 + 8 * b4 + 4 * h);
-            const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-            const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+            for (int b4 = 0; b4 < 4; ++b4) {
+                const float4 l2 = *reinterpret_cast<const float4*>(sL + 8 * b4 + 4 * h);
+                const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int v = 4 * b4 + i;
-                float p = exp2_hw(__builtin_fmaf(s[v], c, -lv[i]));
-                if (edge) {
-                    const int64_t qq = q0 + 8 * b4 + 4 * h + i;
-                    p = (k0 + j <= qq && qq < S) ? p : 0.0f;
+                for (int i = 0; i < 4; ++i) {
+                    const int v = 4 * b4 + i;
+                    float p = exp2_hw(__builtin_fmaf(s[v], c, -lv[i]));
+                    if (edge) p = (lo <= 8 * b4 + i && 8 * b4 + i < hi) ? p : 0.0f;
+                    s[v] = p;
                 }
-                s[v] = p;
-                dp[v] = p * (dp[v] - dv4[i]);
+                pb4[b4 * 64 + lane] = make_float4(s[4 * b4], s[4 * b4 + 1], s[4 * b4 + 2], s[4 * b4 + 3]);
             }
-        }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const bf16x8 pb = pack8(s, u);
-            const bf16x8 sb = pack8(dp, u);
+            for (int u = 0; u < 2; ++u) {
+                const bf16x8 pb = pack8(s, u);
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                dV[db] = mfma(tr_frag(sD, 0, u, db, lane), pb, dV[db]);
-                dK[db] = mfma(tr_frag(sQ, 0, u, db, lane), sb, dK[db]);
+                for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sD, 0, u, db, lane), pb, acc[db]);
+            }
+        } else {
+            f32x16 dp = zero16();
+#pragma unroll
+            for (int st = 0; st < 8; ++st) dp = mfma(row_frag<true>(sD, 0, st, lane), kvf[st], dp);
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4) {
+                const float4 p4 = pb4[b4 * 64 + lane];
+                const float4 d4 = *reinterpret_cast<const float4*>(sL + 32 + 8 * b4 + 4 * h);
+                const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dp[4 * b4 + i] = pv[i] * (dp[4 * b4 + i] - dv[i]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16x8 sb = pack8(dp, u);
+#pragma unroll
+                for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sQ, 0, u, db, lane), sb, acc[db]);
             }
         }
     }
 
     if (k0 + j < S) {
         const int64_t row = ((int64_t)bg * S + k0 + j) * kHeadDim;
-        store_col(a.dk + row, dK, a.scale, h);
-        store_col(a.dv + row, dV, 1.0f, h);
+        if (pwave)
+            store_col(a.dv + row, acc, 1.0f, h);
+        else
+            store_col(a.dk + row, acc, a.scale, h);
     }
 }
 
@@ -344,8 +374,8 @@ constexpr int kDqLoadsPerWave = kTileLoads / kDqWaves;
 
 __device__ __forceinline__ void dq_stage(const uint16_t* kb, const uint16_t* vb, int64_t key0, int64_t last,
                                          char* stage, int w, int lane) {
-    stage_rows<true>(kb, key0, last, stage, w, kDqWaves, 16, lane);
-    stage_rows<false>(vb, key0, last, stage + kKBytes, w, kDqWaves, 16, lane);
+    stage_rows<true>(kb, key0, last, stage, w, kDqWaves, lane);
+    stage_rows<false>(vb, key0, last, stage + kKBytes, w, kDqWaves, lane);
 }
 
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
@@ -429,17 +459,16 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
                 dp[kb] = mfma(row_frag<false>(sV, kb, st, lane), df[st], dp[kb]);
             }
         }
-        // element v of block kb: key key0 + 32 kb + 8 (v >> 2) + 4h + (v & 3), row pos
+        // element v of block kb: key key0 + 32 kb + 8 (v >> 2) + 4h + (v & 3),
+        // visible when that is <= pos, i.e. 32 kb + 8 (v >> 2) + (v & 3) <= vis
         const bool diag = t == t_last;
+        const int vis = (int)(pos - key0) - 4 * h;  // diagonal tile: pos - key0 in [0, 63]
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 float p = exp2_hw(__builtin_fmaf(s[kb][v], c, -lse2));
-                if (diag) {
-                    const int64_t key = key0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-                    p = key <= pos ? p : 0.0f;
-                }
+                if (diag) p = 32 * kb + 8 * (v >> 2) + (v & 3) <= vis ? p : 0.0f;
                 dp[kb][v] = p * (dp[kb][v] - Di);
             }
         }

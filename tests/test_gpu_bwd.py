@@ -13,9 +13,10 @@ bf16-rounded terms (2^-9), computes D_i from the bf16 forward output
 bf16 (2^-9 relative); fp32 accumulation adds far less.  Every term's relative
 error is below 2^-7, so |got - exact| <= 2^-7 e + 2^-8 |exact| element by
 element.  Those roundings have random signs, so the typical error is far
-smaller (measured: mean error 0.3-2% of the mean bound, rms error 0.25% of
-the rms gradient); the test also holds the mean error to a tenth of the mean
-bound and the rms error to 2^-7 of the rms gradient.
+smaller (measured: mean error 0.3-2% of the mean bound), and the test also
+holds the mean error to a tenth of the mean bound.  (A bound relative to the
+gradient's own size does not follow from the roundings: where the sums cancel,
+as with outlier channels, the gradient is small beside its terms.)
 """
 import math
 
@@ -73,12 +74,8 @@ def check_grad(got_bits, ref, budget, what):
     worst = np.unravel_index(int(ratio.argmax()), ratio.shape)
     assert ratio.max() <= 1.0, (f"{what}: error {err[worst]:.3e} at {worst} exceeds {bound[worst]:.3e} "
                                 f"(ref {ref[worst]:.3e}, budget {budget[worst]:.3e})")
-    # typical errors are random-signed roundings, far below the worst case:
-    # mean error within a tenth of the mean bound, rms error within 2^-7 of the rms gradient
+    # typical errors are random-signed roundings, far below the worst case
     assert err.mean() <= 0.1 * bound.mean(), f"{what}: mean error {err.mean():.3e} vs bound {bound.mean():.3e}"
-    rms_ref = math.sqrt(float((ref ** 2).mean()))
-    if rms_ref > 0:
-        assert math.sqrt(float((err ** 2).mean())) <= 2.0 ** -7 * rms_ref, f"{what}: rms error too large"
     return float(ratio.max())
 
 
