@@ -7,7 +7,9 @@ channels x8, V ~ N(0,1), scale 1/sqrt(128)):
   2. partitioned forward of the same rows in 16 chunks of 1024 against the
      cached K/V                                           (prefill_kernel<true>)
   3. one-token decode at context 8192 (split-KV chunks + in-order combine)
-Inputs are resident in HBM before the timed region.  After timing, the
+Inputs are resident in HBM before the timed region.  Outside the step the
+line also reports a decode sweep, a ragged batch, a paged-cache decode and the
+backward of the prefill (each with its own bitwise checks).  After timing, the
 partitioned output and the decode output are compared bit for bit with the
 prefill output.
 
@@ -50,17 +52,27 @@ def prefill_flops(batch: int, n_rows_first_pos: int, n_rows: int) -> int:
     return 4 * D * s * batch * HQ
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources with comments and whitespace removed, so that
-    a counter summary stays valid across edits that change no code."""
+def source_hash(names) -> str:
+    """Hash of kernel sources with comments and whitespace removed, so that a
+    counter summary stays valid across edits that change no code."""
     h = hashlib.sha256()
-    for name in ("kb_attn.hip", "kb_contract.h"):
+    for name in names:
         with open(os.path.join(ROOT, "bitwise_aligned_causal_amd", "csrc", name)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    """Source hash of the forward kernels."""
+    return source_hash(("kb_attn.hip", "kb_contract.h"))
+
+
+def backward_source_hash() -> str:
+    """Source hash of the backward kernels."""
+    return source_hash(("kb_bwd.hip", "kb_contract.h"))
 
 
 def load_traffic(launch_flops: float):
@@ -105,6 +117,49 @@ def cpu_baseline(q, k, v, target_s: float):
                       f"{flops:.3e} FLOPs in {dt:.2f} s"}, rows, ref
 
 
+def backward_section(kb, torch, dev, qd, kd, vd, out_pre, reps: int, check: bool):
+    """The backward of the full causal prefill on the bench input (B=16,
+    S=16384) with a seeded N(0, 1) upstream gradient: prefill_lse, then the
+    backward timed with HIP events on its stream.  FLOPs are the five
+    products' algorithmic count (10*D per visible pair; the dQ kernel's
+    recomputation of S and dP is not counted).  With check: the lse forward's
+    output must equal the plain prefill's bit for bit, and a second backward
+    must reproduce the gradients bit for bit."""
+    import kb_gen
+    import oracle
+
+    stream = torch.cuda.current_stream(dev)
+    do = torch.from_numpy(kb_gen.normal_bf16(SEED, 4, (B, HQ, S, D)).view(np.int16)).to(dev).view(torch.bfloat16)
+    o, lse = kb.prefill_lse(qd, kd, vd)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(kb.backward_workspace_bytes(B, S, HQ, D), dtype=torch.uint8, device=dev)
+    kb.backward(qd, kd, vd, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    times = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(reps):
+        e0.record(stream)
+        kb.backward(qd, kd, vd, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    flops = oracle.backward_flops(B, HQ, S, D)
+    res = {"batch": B, "seq_len": S, "ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 2),
+           "frac_of_peak": round(flops / (ms * 1e-3) / PEAK_BF16, 4), "flops": flops,
+           "flops_count": "5 products x 2*D per visible (query, key) pair"}
+    if check:
+        first = [x.view(torch.int16).clone() for x in (dq, dk, dv)]
+        kb.backward(qd, kd, vd, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws)
+        torch.cuda.synchronize()
+        res["bitwise_mismatch"] = {
+            "lse_forward_vs_prefill": int((o.view(torch.int16) != out_pre.view(torch.int16)).sum()),
+            "rerun": sum(int((a != b.view(torch.int16)).sum()) for a, b in zip(first, (dq, dk, dv)))}
+        del first
+    del do, o, lse, dq, dk, dv, ws
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +171,8 @@ def main() -> int:
                     help="skip the decode sweep and the ragged batch (profiling runs: one kernel configuration each)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--backward-only", type=int, default=0, metavar="N",
+                    help="only run prefill_lse once and the backward N times (profiling runs of the backward)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this operator is built and measured per GPU "
@@ -144,6 +201,10 @@ def main() -> int:
         return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
 
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    if args.backward_only:
+        bwd = backward_section(kb, torch, dev, qd, kd, vd, None, reps=args.backward_only, check=False)
+        print(json.dumps({"backward": bwd}))
+        return 0
     q_chunks = [qd[:, :, c * PART:(c + 1) * PART].contiguous() for c in range(S // PART)]
     q_dec = qd[:, :, DEC_LEN - 1:DEC_LEN].contiguous()
     out_pre = torch.empty_like(qd)
@@ -312,6 +373,7 @@ def main() -> int:
                                                           != out_dec.view(B, HQ, D).view(torch.int16)).sum())}
         del kpool, vpool
     del flush
+    backward = None if args.no_extras else backward_section(kb, torch, dev, qd, kd, vd, out_pre, reps=3, check=True)
 
     pre_ms = float(np.mean(times["pre"]))
     part_ms = float(np.mean(times["part"]))
@@ -351,6 +413,7 @@ def main() -> int:
         "decode_sweep": sweep,
         "varlen": varlen,
         "paged_decode": paged,
+        "backward": backward,
         "bitwise_mismatch": {"partitioned_vs_prefill": mism, "decode_vs_prefill": mism_dec},
         "contract": kb.contract(),
         "kernel_source_hash": kernel_source_hash(),

@@ -8,9 +8,12 @@ The GPU runs (each command runs committed files only):
   rocprofv3 --pmc WRITE_SIZE -d <copy_write> -o run --output-format csv -- python3 bench.py --copy-probe
   rocprofv3 --pmc <8 SQ counters> -d <sqN> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras
       (two passes, SQ_PASSES below)
+  and for the backward kernels, the same --kernel-trace --stats, FETCH_SIZE and
+  WRITE_SIZE runs of `python3 bench.py --backward-only 3`.
 Then, on any host:
   python bench_profile.py --stats <stats> --fetch <fetch> --write <write> \
-      --copy-fetch <copy_fetch> --copy-write <copy_write> [--sq <sq1> <sq2>] --out profiles
+      --copy-fetch <copy_fetch> --copy-write <copy_write> [--sq <sq1> <sq2>] \
+      [--bwd-stats <s> --bwd-fetch <f> --bwd-write <w>] --out profiles
 
 FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  Each is scaled by the
 factor that makes the plain 1 GiB copy read and write exactly 1 GiB.
@@ -42,6 +45,24 @@ KERNELS = {
 }
 
 
+# the backward of the bench's prefill (B=16, S=16384), profiled with
+# `bench.py --backward-only 3` (one prefill_lse launch, four backward calls)
+BWD_KERNELS = {
+    "bwd_dkdv_kernel": ("bwd_dkdv_kernel_b16_s16384", "backward dK, dV of the causal prefill B=16 S=16384"),
+    "bwd_dq_kernel": ("bwd_dq_kernel_b16_s16384", "backward dQ of the causal prefill B=16 S=16384"),
+    "bwd_prep_kernel": ("bwd_prep_kernel_b16_s16384", "backward D_i = <dO_i, O_i> and lse2 per row, B=16 S=16384"),
+}
+BWD_ARGS = "--backward-only 3"
+
+
+def bwd_flops() -> dict:
+    """Products each backward kernel executes, 2*D FLOPs per visible pair each:
+    dK/dV kernel S, dP, dV, dK (4 of the algorithm's 5); dQ kernel dQ plus its
+    recomputation of S and dP (3, of which 1 is new)."""
+    pairs = bench.S * (bench.S + 1) // 2 * bench.B * bench.HQ
+    return {"bwd_dkdv_kernel": 4 * 2 * bench.D * pairs, "bwd_dq_kernel": 3 * 2 * bench.D * pairs}
+
+
 def find_csv(d: str, suffix: str) -> str:
     hits = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
     if not hits:
@@ -49,8 +70,8 @@ def find_csv(d: str, suffix: str) -> str:
     return hits[0]
 
 
-def short(name: str):
-    for k in KERNELS:
+def short(name: str, kernels=None):
+    for k in (kernels or KERNELS):
         if k in name:
             return k
     return None
@@ -109,47 +130,32 @@ def per_counter(d: str):
     return out
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    for a in ("stats", "fetch", "write", "copy_fetch", "copy_write", "out"):
-        ap.add_argument("--" + a.replace("_", "-"), required=True)
-    ap.add_argument("--sq", nargs="*", default=[], help="directories of the SQ counter passes")
-    args = ap.parse_args()
-    f_fetch, f_write = copy_factor(args.copy_fetch), copy_factor(args.copy_write)
-    stats = {}
-    for r in csv.DictReader(open(find_csv(args.stats, "kernel_stats.csv"))):
-        k = short(r["Name"])
-        if k:
-            stats[k] = r
-    fetch, write = per_dispatch(args.fetch), per_dispatch(args.write)
-    src_hash = bench.kernel_source_hash()
-    os.makedirs(args.out, exist_ok=True)
-    for k, (fname, what) in KERNELS.items():
+def write_summaries(kernels, stats, fetch, write, f_fetch, f_write, src_hash, out, stats_args, pmc_args, flops):
+    for k, (fname, what) in kernels.items():
         st = stats.get(k)
-        fr = [v for n, rows in fetch.items() if short(n) == k for v in rows]
-        wr = [v for n, rows in write.items() if short(n) == k for v in rows]
+        fr = [v for n, rows in fetch.items() if short(n, kernels) == k for v in rows]
+        wr = [v for n, rows in write.items() if short(n, kernels) == k for v in rows]
         if not st or not fr or not wr:
             continue
         fetch_kib = statistics.mean(v for _, _, v, _ in fr)
         write_kib = statistics.mean(v for _, _, v, _ in wr)
         hbm = (fetch_kib * f_fetch + write_kib * f_write) * 1024.0
+        avg_us = float(st["AverageNs"]) / 1e3
         lines = [
             f"# {k}: {what}",
             f"kernel source hash (code without comments): {src_hash}",
             "",
             "commands:",
-            "  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras",
-            "  rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- "
-            "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras",
-            "  rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- "
-            "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras",
+            f"  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- python3 bench.py {stats_args}",
+            f"  rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- python3 bench.py {pmc_args}",
+            f"  rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- python3 bench.py {pmc_args}",
             "  rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE ... -- python3 bench.py --copy-probe   (1 GiB copy)",
             "  python bench_profile.py --stats <stats> --fetch <fetch> --write <write> "
-            "--copy-fetch <copy_fetch> --copy-write <copy_write> --out profiles",
+            "--copy-fetch <copy_fetch> --copy-write <copy_write> "
+            "[--bwd-stats <s> --bwd-fetch <f> --bwd-write <w>] --out profiles",
             "",
             "kernel-trace --stats:",
-            f"  calls {st['Calls']}, average {float(st['AverageNs']) / 1e3:.1f} us, "
+            f"  calls {st['Calls']}, average {avg_us:.1f} us, "
             f"min {float(st['MinNs']) / 1e3:.1f} us, max {float(st['MaxNs']) / 1e3:.1f} us, "
             f"{float(st['Percentage']):.2f} % of GPU time",
             "",
@@ -159,15 +165,48 @@ def main():
             f"writes {COPY_BYTES / 1024 / f_write:.0f} KiB -> factors fetch x{f_fetch:.3f}, write x{f_write:.3f}",
             f"  HBM bytes per dispatch (scaled): {hbm:.4e}",
         ]
-        with open(os.path.join(args.out, fname + ".txt"), "w") as fh:
+        if k in flops:
+            lines += ["", f"executed MFMA FLOPs per dispatch: {flops[k]:.4e} -> "
+                          f"{flops[k] / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s at the average duration "
+                          f"({flops[k] / (avg_us * 1e-6) / bench.PEAK_BF16:.3f} of the 2.5 PFLOP/s bf16 peak)"]
+        with open(os.path.join(out, fname + ".txt"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
         rec = {"kernel": k, "workload": what, "kernel_source_hash": src_hash, "fetch_kib": fetch_kib,
                "write_kib": write_kib, "fetch_factor": f_fetch, "write_factor": f_write,
-               "hbm_bytes_per_launch": hbm, "avg_duration_us": float(st["AverageNs"]) / 1e3,
-               "calls_in_stats_run": int(st["Calls"])}
-        with open(os.path.join(args.out, fname + "_traffic.json"), "w") as fh:
+               "hbm_bytes_per_launch": hbm, "avg_duration_us": avg_us, "calls_in_stats_run": int(st["Calls"])}
+        with open(os.path.join(out, fname + "_traffic.json"), "w") as fh:
             json.dump(rec, fh, indent=1)
-        print(f"{k}: avg {rec['avg_duration_us']:.1f} us, HBM {hbm:.3e} B/launch")
+        print(f"{k}: avg {avg_us:.1f} us, HBM {hbm:.3e} B/launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    for a in ("stats", "fetch", "write", "copy_fetch", "copy_write", "out"):
+        ap.add_argument("--" + a.replace("_", "-"), required=True)
+    ap.add_argument("--sq", nargs="*", default=[], help="directories of the SQ counter passes")
+    for a in ("bwd_stats", "bwd_fetch", "bwd_write"):
+        ap.add_argument("--" + a.replace("_", "-"), default=None,
+                        help="rocprofv3 output of bench.py --backward-only 3 (stats, FETCH_SIZE, WRITE_SIZE)")
+    args = ap.parse_args()
+    f_fetch, f_write = copy_factor(args.copy_fetch), copy_factor(args.copy_write)
+    stats = {}
+    for r in csv.DictReader(open(find_csv(args.stats, "kernel_stats.csv"))):
+        k = short(r["Name"])
+        if k:
+            stats[k] = r
+    src_hash = bench.kernel_source_hash()
+    os.makedirs(args.out, exist_ok=True)
+    write_summaries(KERNELS, stats, per_dispatch(args.fetch), per_dispatch(args.write), f_fetch, f_write, src_hash,
+                    args.out, "--steps 3 --warmup 1 --no-cpu-baseline --no-extras",
+                    "--steps 1 --warmup 0 --no-cpu-baseline --no-extras", {})
+    if args.bwd_stats:
+        bstats = {}
+        for r in csv.DictReader(open(find_csv(args.bwd_stats, "kernel_stats.csv"))):
+            k = short(r["Name"], BWD_KERNELS)
+            if k:
+                bstats[k] = r
+        write_summaries(BWD_KERNELS, bstats, per_dispatch(args.bwd_fetch), per_dispatch(args.bwd_write), f_fetch,
+                        f_write, bench.backward_source_hash(), args.out, BWD_ARGS, BWD_ARGS, bwd_flops())
     if args.sq:
         sq_summary(args.sq, args.out, src_hash)
 
