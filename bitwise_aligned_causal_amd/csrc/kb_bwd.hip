@@ -67,6 +67,15 @@ __device__ __forceinline__ void stage_rows(const uint16_t* base, int64_t row0, i
     }
 }
 
+// lds_dma16 with the scalar base forced into scalar registers: the base is
+// uniform by construction, but the compiler cannot always prove it.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, char* dst) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    lds_dma16(reinterpret_cast<const char*>((uintptr_t)(((uint64_t)hi << 32) | lo)), voff, dst);
+}
+
 // Row fragment: lane (row 32 blk + (lane & 31), half h) holds bf16
 // [16 st + 8h, 16 st + 8h + 7] of its row -- the A operand of a product whose
 // rows are the tile's rows, or the B operand whose columns are.
@@ -197,10 +206,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 //   dS-wave (w >= 4)  one item later: dP = dO V^T, P from LDS,
 //                     dS = P (dP - D), dK^T += Q^T dS
 // so each wave holds one accumulator set (64 registers) and one of K, V.
-// Work items t = 0, 1, ...: query tile q0 = K0 + 32 (t / 4) of query head
-// 4g + (t % 4).  A 4-stage LDS ring holds each item's Q rows, dO rows (dual
-// swizzle) and its 32 lse2 and 32 D values, loaded two items ahead; P goes
-// through a double buffer.  dK^T and dV^T accumulate over the items in order.
+// Work items t = 0, 1, ...: query tile q0 = qlast - 32 (t / 4) of query head
+// 4g + (t % 4), from the last tile qlast down to K0.  A 4-stage LDS ring holds
+// each item's Q rows, dO rows (dual swizzle) and its 32 lse2 and 32 D values,
+// loaded two items ahead; P goes through a double buffer.  dK^T and dV^T
+// accumulate over the items in that fixed order.
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 8;
 constexpr int kKvKeys = 128;
@@ -210,9 +220,9 @@ constexpr int kKvStages = 4;
 constexpr int kPBufBytes = 4 * 4096;                  // fp32 P of the 4 key groups
 constexpr int kKvLoadsPerWave = (2 * kQTileBytes / 1024) / kKvWaves + 1;  // 2 tile loads + 1 block of 8 floats
 
-__device__ __forceinline__ void kv_stage(const BwdArgs& a, int64_t bh0, int t, int64_t K0, char* stage, int w,
+__device__ __forceinline__ void kv_stage(const BwdArgs& a, int64_t bh0, int t, int64_t qlast, char* stage, int w,
                                          int lane) {
-    const int64_t q0 = K0 + 32 * (t >> 2);
+    const int64_t q0 = qlast - 32 * (t >> 2);
     const int64_t bh = bh0 + (t & 3);  // (sequence, query head) row block
     const char* qb = reinterpret_cast<const char*>(a.q + (bh * a.seq_len + q0) * kHeadDim);
     const char* db = reinterpret_cast<const char*>(a.dout + (bh * a.seq_len + q0) * kHeadDim);
@@ -224,12 +234,120 @@ __device__ __forceinline__ void kv_stage(const BwdArgs& a, int64_t bh0, int t, i
         const int row = 4 * (i & 7) + (lane >> 4);
         const int c = (lane & 15) ^ dual_swz(row);
         const int64_t r = row < last ? row : last;
-        lds_dma16(i < 8 ? qb : db, (uint32_t)(r * 256 + c * 16), stage + 1024 * i);
+        dma16(i < 8 ? qb : db, (uint32_t)(r * 256 + c * 16), stage + 1024 * i);
     }
     // lse2 / D of the 32 rows (padded arrays, in bounds): wave w moves 8
     // floats with lanes 0..1 (w < 4: lse2[8w ..], else D[8(w-4) ..])
     const float* src = (w < 4 ? a.ws_lse2 : a.ws_d) + bh * a.s_pad + q0 + 8 * (w & 3);
-    if (lane < 2) lds_dma16(reinterpret_cast<const char*>(src), (uint32_t)(lane * 16), stage + 2 * kQTileBytes + 32 * w);
+    if (lane < 2) dma16(reinterpret_cast<const char*>(src), (uint32_t)(lane * 16), stage + 2 * kQTileBytes + 32 * w);
+}
+
+// Everything a dK/dV wave needs once its work item is known.
+struct KvWork {
+    int64_t S, K0, k0, bh0, qlast;
+    int n_items, kg, w, lane;
+    char* smem;
+    char* pbuf;
+};
+
+// P-wave part of one item: S = Q K^T, P (masked on edge tiles), P to LDS,
+// dV^T += dO^T P.  Element v: query q0 + 8 (v >> 2) + 4h + (v & 3), key
+// k0 + j; on an edge tile it counts when k0 + j <= query < S, i.e.
+// lo <= 8 (v >> 2) + (v & 3) < hi.  The mask is a uniform branch around the
+// selects only, so the accumulators never cross a join.
+__device__ __forceinline__ void p_item(const bf16x8 (&kf)[8], const char* sQ, const char* sD, const float* sL,
+                                       float4* pb4, int lane, float c, bool edge, int lo, int hi,
+                                       f32x16 (&acc)[4]) {
+    const int h = lane >> 5;
+    f32x16 s = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st) s = mfma(row_frag<true>(sQ, 0, st, lane), kf[st], s);
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4) {
+        const float4 l2 = *reinterpret_cast<const float4*>(sL + 8 * b4 + 4 * h);
+        const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[4 * b4 + i] = exp2_hw(__builtin_fmaf(s[4 * b4 + i], c, -lv[i]));
+    }
+    if (edge) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int off = 8 * (v >> 2) + (v & 3);
+            s[v] = (lo <= off && off < hi) ? s[v] : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4)
+        pb4[b4 * 64 + lane] = make_float4(s[4 * b4], s[4 * b4 + 1], s[4 * b4 + 2], s[4 * b4 + 3]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const bf16x8 pb = pack8(s, u);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sD, 0, u, db, lane), pb, acc[db]);
+    }
+}
+
+// dS-wave part of one item: dP = dO V^T, P from LDS, dS = P (dP - D),
+// dK^T += Q^T dS.
+__device__ __forceinline__ void ds_item(const bf16x8 (&vf)[8], const char* sQ, const char* sD, const float* sL,
+                                        const float4* pb4, int lane, f32x16 (&acc)[4]) {
+    const int h = lane >> 5;
+    f32x16 dp = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st) dp = mfma(row_frag<true>(sD, 0, st, lane), vf[st], dp);
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4) {
+        const float4 p4 = pb4[b4 * 64 + lane];
+        const float4 d4 = *reinterpret_cast<const float4*>(sL + 32 + 8 * b4 + 4 * h);
+        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dp[4 * b4 + i] = pv[i] * (dp[4 * b4 + i] - dv[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const bf16x8 sb = pack8(dp, u);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sQ, 0, u, db, lane), sb, acc[db]);
+    }
+}
+
+// The item loop of one role (both roles run the same iterations and
+// barriers; the P-wave works on item t, the dS-wave on item t - 1).  Each
+// role has its own loop so that its accumulators stay in place.
+template <bool kP>
+__device__ __forceinline__ void kv_loop(const BwdArgs& a, const KvWork& wk, const bf16x8 (&kvf)[8],
+                                        f32x16 (&acc)[4]) {
+    const int lane = wk.lane, j = lane & 31, h = lane >> 5;
+    const float c = a.c;
+    for (int t = 0; t <= wk.n_items; ++t) {
+        // publish item t's stage (the item t + 1 stage may still be loading), refill
+        if (t + 1 < wk.n_items)
+            wait_vm<kKvLoadsPerWave>();
+        else
+            wait_vm<0>();
+        __syncthreads();
+        if (t + 2 < wk.n_items)
+            kv_stage(a, wk.bh0, t + 2, wk.qlast, wk.smem + ((t + 2) % kKvStages) * kKvStageBytes, wk.w, lane);
+
+        const int it = kP ? t : t - 1;
+        if (it < 0 || it >= wk.n_items) continue;
+        const int64_t q0 = wk.qlast - 32 * (it >> 2);
+        if (q0 < wk.k0) continue;  // every key of this group lies after every row of the tile
+        const char* stage = wk.smem + (it % kKvStages) * kKvStageBytes;
+        const char* sQ = stage;
+        const char* sD = stage + kQTileBytes;
+        const float* sL = reinterpret_cast<const float*>(stage + 2 * kQTileBytes);
+        float4* pb4 = reinterpret_cast<float4*>(wk.pbuf + (it & 1) * kPBufBytes + wk.kg * 4096);
+        if (kP) {
+            const bool edge = q0 == wk.k0 || q0 + 32 > wk.S;
+            const int lo = (int)(wk.k0 - q0) + j - 4 * h;
+            const int hi = (int)(wk.S - q0 < 64 ? wk.S - q0 : 64) - 4 * h;
+            p_item(kvf, sQ, sD, sL, pb4, lane, c, edge, lo, hi, acc);
+        } else {
+            ds_item(kvf, sQ, sD, sL, pb4, lane, acc);
+        }
+    }
 }
 
 __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
@@ -246,8 +364,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     int bg, kb;
     if ((nbg & 7) == 0) {
         // XCD k (x % 8) takes the (b, g) pairs k, k + 8, ..., each pair's key
-        // blocks longest work first, so the blocks of one pair share the
-        // Q / dO stream in that XCD's L2
+        // blocks longest work first
         const int i = x >> 3;
         bg = (i / n_kb) * 8 + (x & 7);
         kb = i % n_kb;
@@ -256,21 +373,31 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
         kb = x / nbg;
     }
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
-    const int64_t S = a.seq_len;
-    const int64_t K0 = (int64_t)kb * kKvKeys;
-    const int64_t k0 = K0 + 32 * kg;  // this wave's first key
-    const int64_t bh0 = (int64_t)b * kGroup * a.n_kv_heads + kGroup * g;
-    const int n_items = 4 * (int)((S - K0 + 31) / 32);
-    char* pbuf = smem + kKvStages * kKvStageBytes;
+    KvWork wk;
+    wk.S = a.seq_len;
+    wk.K0 = (int64_t)kb * kKvKeys;
+    wk.k0 = wk.K0 + 32 * kg;  // this wave's first key
+    wk.bh0 = (int64_t)b * kGroup * a.n_kv_heads + kGroup * g;
+    // query tiles from the last one down to K0: every block of a (sequence,
+    // KV head) starts at the same rows, so the blocks running together on an
+    // XCD read the same Q / dO rows at about the same time (one L2 fetch)
+    wk.qlast = ((wk.S - 1) >> 5) << 5;
+    wk.n_items = 4 * (int)((wk.qlast - wk.K0) / 32 + 1);
+    wk.kg = kg;
+    wk.w = w;
+    wk.lane = lane;
+    wk.smem = smem;
+    wk.pbuf = smem + kKvStages * kKvStageBytes;
+    const int64_t S = wk.S;
 
-    kv_stage(a, bh0, 0, K0, smem, w, lane);
-    if (n_items >= 2) kv_stage(a, bh0, 1, K0, smem + kKvStageBytes, w, lane);
+    kv_stage(a, wk.bh0, 0, wk.qlast, smem, w, lane);
+    if (wk.n_items >= 2) kv_stage(a, wk.bh0, 1, wk.qlast, smem + kKvStageBytes, w, lane);
 
     // this wave's K (P-wave) or V (dS-wave) rows as B operands: lane (key j,
     // half h) holds row k0 + j, d = 16 st + 8h .. + 7 (rows beyond S read row S - 1)
     bf16x8 kvf[8];
     {
-        int64_t key = k0 + j;
+        int64_t key = wk.k0 + j;
         key = key < S ? key : S - 1;
         const uint16_t* src = (pwave ? a.k : a.v) + ((int64_t)bg * S + key) * kHeadDim;
 #pragma unroll
@@ -281,84 +408,13 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     f32x16 acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = zero16();
-    const float c = a.c;
-
-    for (int t = 0; t <= n_items; ++t) {
-        // publish item t's stage (the item t + 1 stage may still be loading), refill
-        if (t + 1 < n_items)
-            wait_vm<kKvLoadsPerWave>();
-        else
-            wait_vm<0>();
-        __syncthreads();
-        if (t + 2 < n_items) kv_stage(a, bh0, t + 2, K0, smem + ((t + 2) % kKvStages) * kKvStageBytes, w, lane);
-
-        // the P-wave works on item t, the dS-wave on item t - 1
-        const int it = pwave ? t : t - 1;
-        if (it < 0 || it >= n_items) continue;
-        const int64_t q0 = K0 + 32 * (it >> 2);
-        if (q0 < k0) continue;  // every key of this group lies after every row of the tile
-        const char* stage = smem + (it % kKvStages) * kKvStageBytes;
-        const char* sQ = stage;
-        const char* sD = stage + kQTileBytes;
-        const float* sL = reinterpret_cast<const float*>(stage + 2 * kQTileBytes);
-        float4* pb4 = reinterpret_cast<float4*>(pbuf + (it & 1) * kPBufBytes + kg * 4096);
-
-        if (pwave) {
-            f32x16 s = zero16();
-#pragma unroll
-            for (int st = 0; st < 8; ++st) s = mfma(row_frag<true>(sQ, 0, st, lane), kvf[st], s);
-            // element v: query q0 + 8 (v >> 2) + 4h + (v & 3), key k0 + j; it
-            // counts when k0 + j <= query < S, i.e. lo <= 8 (v >> 2) + (v & 3) < hi
-            const bool edge = (q0 == k0) || (q0 + 32 > S);
-            const int lo = (int)(k0 - q0) + j - 4 * h;
-            const int hi = (int)(S - q0 < 64 ? S - q0 : 64) - 4 * h;
-#pragma unroll
-            for (int b4 = 0; b4 < 4; ++b4) {
-                const float4 l2 = *reinterpret_cast<const float4*>(sL + 8 * b4 + 4 * h);
-                const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int v = 4 * b4 + i;
-                    float p = exp2_hw(__builtin_fmaf(s[v], c, -lv[i]));
-                    if (edge) p = (lo <= 8 * b4 + i && 8 * b4 + i < hi) ? p : 0.0f;
-                    s[v] = p;
-                }
-                pb4[b4 * 64 + lane] = make_float4(s[4 * b4], s[4 * b4 + 1], s[4 * b4 + 2], s[4 * b4 + 3]);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8 pb = pack8(s, u);
-#pragma unroll
-                for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sD, 0, u, db, lane), pb, acc[db]);
-            }
-        } else {
-            f32x16 dp = zero16();
-#pragma unroll
-            for (int st = 0; st < 8; ++st) dp = mfma(row_frag<true>(sD, 0, st, lane), kvf[st], dp);
-#pragma unroll
-            for (int b4 = 0; b4 < 4; ++b4) {
-                const float4 p4 = pb4[b4 * 64 + lane];
-                const float4 d4 = *reinterpret_cast<const float4*>(sL + 32 + 8 * b4 + 4 * h);
-                const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
-                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dp[4 * b4 + i] = pv[i] * (dp[4 * b4 + i] - dv[i]);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8 sb = pack8(dp, u);
-#pragma unroll
-                for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sQ, 0, u, db, lane), sb, acc[db]);
-            }
-        }
-    }
-
-    if (k0 + j < S) {
-        const int64_t row = ((int64_t)bg * S + k0 + j) * kHeadDim;
-        if (pwave)
-            store_col(a.dv + row, acc, 1.0f, h);
-        else
-            store_col(a.dk + row, acc, a.scale, h);
+    const int64_t row = ((int64_t)bg * S + wk.k0 + j) * kHeadDim;
+    if (pwave) {
+        kv_loop<true>(a, wk, kvf, acc);
+        if (wk.k0 + j < S) store_col(a.dv + row, acc, 1.0f, h);
+    } else {
+        kv_loop<false>(a, wk, kvf, acc);
+        if (wk.k0 + j < S) store_col(a.dk + row, acc, a.scale, h);
     }
 }
 
@@ -459,18 +515,26 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
                 dp[kb] = mfma(row_frag<false>(sV, kb, st, lane), df[st], dp[kb]);
             }
         }
-        // element v of block kb: key key0 + 32 kb + 8 (v >> 2) + 4h + (v & 3),
-        // visible when that is <= pos, i.e. 32 kb + 8 (v >> 2) + (v & 3) <= vis
-        const bool diag = t == t_last;
-        const int vis = (int)(pos - key0) - 4 * h;  // diagonal tile: pos - key0 in [0, 63]
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float p = exp2_hw(__builtin_fmaf(s[kb][v], c, -lse2));
-                if (diag) p = 32 * kb + 8 * (v >> 2) + (v & 3) <= vis ? p : 0.0f;
-                dp[kb][v] = p * (dp[kb][v] - Di);
+            for (int v = 0; v < 16; ++v) s[kb][v] = exp2_hw(__builtin_fmaf(s[kb][v], c, -lse2));
+        }
+        // diagonal tile only (a uniform branch around the selects): element v
+        // of block kb is key key0 + 32 kb + 8 (v >> 2) + 4h + (v & 3), visible
+        // when that is <= pos, i.e. 32 kb + 8 (v >> 2) + (v & 3) <= vis
+        if (t == t_last) {
+            const int vis = (int)(pos - key0) - 4 * h;  // pos - key0 in [0, 63]
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[kb][v] = 32 * kb + 8 * (v >> 2) + (v & 3) <= vis ? s[kb][v] : 0.0f;
             }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dp[kb][v] = s[kb][v] * (dp[kb][v] - Di);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
