@@ -220,3 +220,47 @@ def test_backward_full_size_sampled():
     dos = kb_gen.bf16_bits_to_f32(do).astype(np.float64).reshape(B, HKV, 4, S, D).sum(axis=(2, 3))
     scale_v = np.abs(dvf).sum(axis=2)
     assert np.all(np.abs(sv - dos) <= 2.0 ** -6 * scale_v), "sum_j dV_j differs from the summed dO"
+
+
+@pytest.mark.parametrize("hq,hkv,S,scale", [(4, 1, 129, 0.05), (8, 2, 70, None), (12, 3, 257, 0.2)])
+def test_backward_other_heads_and_scale(hq, hkv, S, scale):
+    m = kb()
+    q = kb_gen.normal_bf16(300 + S, 1, (1, hq, S, D))
+    k = kb_gen.normal_bf16(300 + S, 2, (1, hkv, S, D))
+    v = kb_gen.normal_bf16(300 + S, 3, (1, hkv, S, D))
+    do = kb_gen.normal_bf16(300 + S, 4, (1, hq, S, D))
+    Q, K, V, DO = dev(q), dev(k), dev(v), dev(do)
+    note(f"backward Hq={hq} Hkv={hkv} S={S} scale={scale}")
+    o, lse = m.prefill_lse(Q, K, V, scale)
+    dq, dk, dv = m.backward(Q, K, V, o, DO, lse, scale)
+    sc = SCALE if scale is None else scale
+    check_lse(gpu_lse(lse), oracle.lse(q, k, v, scale=sc, threads=oracle_threads()), f"lse Hq={hq}")
+    ref = oracle.backward(q, k, v, do, scale=sc, budgets=True, threads=oracle_threads())
+    check_grad(bits(dq), ref["dq"], ref["eq"], f"dq Hq={hq}")
+    check_grad(bits(dk), ref["dk"], ref["ek"], f"dk Hq={hq}")
+    check_grad(bits(dv), ref["dv"], ref["ev"], f"dv Hq={hq}")
+
+
+def test_backward_from_partitioned_forward_is_bitwise_the_same():
+    """o and lse assembled from partitioned chunks give the prefill-based
+    gradients bit for bit (the forward contract makes both inputs identical)."""
+    import torch
+
+    m = kb()
+    B, S = 2, 1500
+    q, k, v, do = make(31, B, S)
+    Q, K, V, DO = dev(q), dev(k), dev(v), dev(do)
+    note("backward from prefill_lse vs from partitioned_lse chunks")
+    o, lse = m.prefill_lse(Q, K, V)
+    ref = [bits(x) for x in m.backward(Q, K, V, o, DO, lse)]
+    outs, lses, start = [], [], 0
+    for stop in (513, 1024, 1100, S):
+        oc, lc = m.partitioned_lse(Q[:, :, start:stop].contiguous(), K, V, stop)
+        outs.append(oc)
+        lses.append(lc)
+        start = stop
+    o2 = torch.cat(outs, dim=2).contiguous()
+    lse2 = torch.cat(lses, dim=2).contiguous()
+    got = [bits(x) for x in m.backward(Q, K, V, o2, DO, lse2)]
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert np.array_equal(a, b), name
