@@ -148,12 +148,21 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
         for (int db = 0; db < 4; ++db) acc[db] = zero16();
     };
 
-    // tiles below the diagonal: every key visible to every row
-    for (int t = 0; t < t_last; ++t) {
-        publish(t);
-        const char* buf = smem + (t % kStages) * kTileBytes;
-        tile_step<4, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, 0);
-        if ((t % kTilesPerChunk) == kTilesPerChunk - 1) close_chunk();
+    // tiles below the diagonal: every key visible to every row; chunk by
+    // chunk, the first tile of each peeled (it starts from zero accumulators)
+    for (int t0 = 0; t0 < t_last; t0 += kTilesPerChunk) {
+        {
+            publish(t0);
+            const char* buf = smem + (t0 % kStages) * kTileBytes;
+            tile_step<4, false, true>(qf, buf, buf + kKBytes, lane, (int64_t)t0 * kTile, pos, c, mc, l, acc, 0);
+        }
+        const int t_end = min(t0 + kTilesPerChunk, t_last);
+        for (int t = t0 + 1; t < t_end; ++t) {
+            publish(t);
+            const char* buf = smem + (t % kStages) * kTileBytes;
+            tile_step<4, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, 0);
+        }
+        if (t_end == t0 + kTilesPerChunk) close_chunk();
     }
     // the diagonal tile t_last holds keys beyond some rows' positions
     {

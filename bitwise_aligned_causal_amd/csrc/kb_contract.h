@@ -435,7 +435,11 @@ __device__ __forceinline__ void pv_step(const bf16x8& pf, const char* sV, int kb
 // holds keys beyond some column's position).  The arithmetic is that of
 // sm_tile + rescale_o + pv_tile; P is produced one 16-key step at a time so
 // that a step's P V products can run beside the next step's exponentials.
-template <int NDB, bool kMask>
+// kFirst marks the first tile of a chunk (mc = -inf, l = 0, o = 0 on entry):
+// its reference max always moves and a = 0, and o * 0 = +0 = o, so the
+// rescale is skipped and the products start from a zero accumulator -- the
+// same bits as the general form.
+template <int NDB, bool kMask, bool kFirst = false>
 __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
                                           int64_t key0, int64_t pos, float c, float& mc, float& l,
                                           f32x16 (&o)[NDB], int dblk0) {
@@ -469,7 +473,12 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
     bf16x8 pf[2][2];
     float part[2][2];
     p_step(s0, 0, c, nmc, pf[0][0], part[0][0]);
-    rescale_o<NDB>(o, a, any_grow);
+    if (kFirst) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = zero16();
+    } else {
+        rescale_o<NDB>(o, a, any_grow);
+    }
     pv_step<NDB>(pf[0][0], sV, 0, 0, lane, o, dblk0);
     p_step(s0, 1, c, nmc, pf[0][1], part[0][1]);
     pv_step<NDB>(pf[0][1], sV, 0, 1, lane, o, dblk0);
