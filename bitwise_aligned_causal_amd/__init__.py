@@ -17,6 +17,7 @@ Entry points (KernelBraid / AReaL-TIK README, "Usage" and "Method"):
   prefill_lse / partitioned_lse / decode_lse
                                             the same, also returning each row's log-sum-exp
   backward(q, k, v, out, dout, lse)         deterministic dq, dk, dv of the causal prefill
+  prefill_varlen_lse / backward_varlen      the same for ragged (packed) batches
   attention(q, k, v)                        differentiable prefill (autograd glue)
 All forward entry points give bitwise-identical rows (and log-sum-exps) for
 the same inputs and context.
@@ -86,6 +87,13 @@ def lib() -> ctypes.CDLL:
         L.kb_attn_backward.restype = ctypes.c_int
         L.kb_attn_backward_workspace_bytes.argtypes = [i64, i64, i32, i32]
         L.kb_attn_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.kb_attn_prefill_varlen_lse.argtypes = [vp, vp, vp, vp, vp, p64, i64, i32, i32, i32, f32, vp]
+        L.kb_attn_prefill_varlen_lse.restype = ctypes.c_int
+        L.kb_attn_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, p64, i64, i32, i32, i32, f32, vp,
+                                              ctypes.c_size_t, vp]
+        L.kb_attn_backward_varlen.restype = ctypes.c_int
+        L.kb_attn_backward_varlen_workspace_bytes.argtypes = [p64, i64, i32, i32]
+        L.kb_attn_backward_varlen_workspace_bytes.restype = ctypes.c_size_t
         L.kb_attn_strerror.argtypes = [ctypes.c_int]
         L.kb_attn_strerror.restype = ctypes.c_char_p
         L.kb_attn_contract.argtypes = [ctypes.POINTER(i32)] * 3
@@ -401,6 +409,63 @@ def backward(q, k, v, out, dout, lse, scale: float | None = None, dq=None, dk=No
     return dq, dk, dv
 
 
+def prefill_varlen_lse(q, k, v, cu_seqlens, scale: float | None = None, out=None, lse=None):
+    """prefill_varlen() that also returns the fp32 log-sum-exp of every row, [Hq, T]."""
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _check_packed(n, x)
+    if k.shape != v.shape or k.shape[1] != q.shape[1]:
+        raise ValueError("k/v must be [Hkv, T, 128] with the rows of q")
+    if int(cu_seqlens[-1]) != q.shape[1]:
+        raise ValueError("cu_seqlens[-1] must equal the packed row count")
+    cu = _host_i64(cu_seqlens)
+    out = _torch().empty_like(q) if out is None else out
+    _check_packed("out", out)
+    lse = _lse_out(lse, (q.shape[0], q.shape[1]), q)
+    check(lib().kb_attn_prefill_varlen_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                           cu, len(cu_seqlens) - 1, q.shape[0], k.shape[0], HEAD_DIM,
+                                           _scale(scale, HEAD_DIM), _stream(q)))
+    return out, lse
+
+
+def backward_varlen_workspace_bytes(cu_seqlens, n_q_heads: int = 32, head_dim: int = HEAD_DIM) -> int:
+    cu = _host_i64(cu_seqlens)
+    return int(lib().kb_attn_backward_varlen_workspace_bytes(cu, len(cu_seqlens) - 1, n_q_heads, head_dim))
+
+
+def backward_varlen(q, k, v, out, dout, lse, cu_seqlens, scale: float | None = None, dq=None, dk=None, dv=None,
+                    workspace=None):
+    """Gradients of the ragged causal prefill: packed q, out, dout [Hq, T,
+    128], k, v [Hkv, T, 128], lse [Hq, T] from prefill_varlen_lse; sequence i
+    is rows cu_seqlens[i] .. cu_seqlens[i+1] - 1 (host list)."""
+    torch = _torch()
+    for n, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_packed(n, x)
+    T = q.shape[1]
+    if k.shape != v.shape or k.shape[1] != T or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("packed shapes do not match")
+    if int(cu_seqlens[-1]) != T:
+        raise ValueError("cu_seqlens[-1] must equal the packed row count")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda
+            or tuple(lse.shape) != (q.shape[0], T) or not lse.is_contiguous()):
+        raise ValueError("lse must be the contiguous float32 [Hq, T] tensor of the forward")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_packed(n, x)
+    need = backward_varlen_workspace_bytes(cu_seqlens, q.shape[0])
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    cu = _host_i64(cu_seqlens)
+    check(lib().kb_attn_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu,
+                                        len(cu_seqlens) - 1, q.shape[0], k.shape[0], HEAD_DIM,
+                                        _scale(scale, HEAD_DIM), ws_ptr, ws_bytes, _stream(q)))
+    return dq, dk, dv
+
+
 def attention(q, k, v, scale: float | None = None):
     """Differentiable causal attention: forward through prefill_lse, backward
     through backward (torch autograd glue only)."""
@@ -438,4 +503,5 @@ def unified_decode(q_last, k, v, H_Q: int, H_KV: int, scale: float | None = None
 __all__ = ["prefill", "partitioned", "decode", "unified_prefill", "unified_decode", "contract",
            "decode_workspace_bytes", "prefill_varlen", "partitioned_varlen", "decode_varlen",
            "decode_varlen_workspace_bytes", "decode_paged", "prefill_lse", "partitioned_lse", "decode_lse",
-           "backward", "backward_workspace_bytes", "attention", "lib", "check", "KBAttnError", "LIB_PATH"]
+           "backward", "backward_workspace_bytes", "prefill_varlen_lse", "backward_varlen",
+           "backward_varlen_workspace_bytes", "attention", "lib", "check", "KBAttnError", "LIB_PATH"]

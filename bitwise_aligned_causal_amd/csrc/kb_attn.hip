@@ -244,6 +244,7 @@ struct VarlenArgs {
     const uint16_t* k;
     const uint16_t* v;
     uint16_t* o;
+    float* lse;               // optional: [Hq, q_rows] log-sum-exp of each row
     int64_t q_rows, kv_rows;  // rows per head of the packed tensors
     int32_t n_kv_heads;
     float c;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_varlen_kernel(Varl
     PrefillWork wk;
     wk.q0 = a.q + ((int64_t)kGroup * g * a.q_rows + t.q_row0[s]) * kHeadDim;
     wk.o0 = a.o + ((int64_t)kGroup * g * a.q_rows + t.q_row0[s]) * kHeadDim;
-    wk.lse0 = nullptr;
+    wk.lse0 = a.lse ? a.lse + (int64_t)kGroup * g * a.q_rows + t.q_row0[s] : nullptr;
     wk.q_hstride = a.q_rows;
     wk.kbase = a.k + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
     wk.vbase = a.v + ((int64_t)g * a.kv_rows + t.kv_row0[s]) * kHeadDim;
@@ -684,7 +685,7 @@ int read_ragged(const int64_t* cu_q, const int64_t* cu_kv, const int64_t* kv_len
     return KB_ATTN_OK;
 }
 
-int launch_prefill_varlen(const void* q, const void* k, const void* v, void* o, std::vector<RaggedSeq> seqs,
+int launch_prefill_varlen(const void* q, const void* k, const void* v, void* o, float* lse, std::vector<RaggedSeq> seqs,
                           int64_t q_rows, int64_t kv_rows, int32_t n_kv_heads, float scale, hipStream_t stream) {
     // longest sequences first, so the longest position blocks start first
     std::stable_sort(seqs.begin(), seqs.end(),
@@ -694,6 +695,7 @@ int launch_prefill_varlen(const void* q, const void* k, const void* v, void* o, 
     a.k = (const uint16_t*)k;
     a.v = (const uint16_t*)v;
     a.o = (uint16_t*)o;
+    a.lse = lse;
     a.q_rows = q_rows;
     a.kv_rows = kv_rows;
     a.n_kv_heads = n_kv_heads;
@@ -960,7 +962,28 @@ int kb_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
         ranges_overlap(o, qbytes, v, kvbytes))
         return KB_ATTN_ERR_ALIAS;
     if (int rc = check_device({q, k, v, o})) return rc;
-    return launch_prefill_varlen(q, k, v, o, seqs, q_rows, kv_rows, n_kv_heads, scale, stream);
+    return launch_prefill_varlen(q, k, v, o, nullptr, seqs, q_rows, kv_rows, n_kv_heads, scale, stream);
+}
+
+int kb_attn_prefill_varlen_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int64_t* cu_seqlens, int64_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, float scale, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !cu_seqlens || batch < 1) return KB_ATTN_ERR_INVALID_ARG;
+    if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
+    if (int rc = check_scale(scale)) return rc;
+    std::vector<RaggedSeq> seqs;
+    int64_t q_rows = 0, kv_rows = 0;
+    if (int rc = read_ragged(cu_seqlens, cu_seqlens, nullptr, batch, seqs, q_rows, kv_rows)) return rc;
+    if (int rc = check_aligned({q, k, v, o})) return rc;
+    const size_t qbytes = (size_t)n_q_heads * q_rows * kHeadDim * 2;
+    const size_t kvbytes = (size_t)n_kv_heads * kv_rows * kHeadDim * 2;
+    if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k, kvbytes) ||
+        ranges_overlap(o, qbytes, v, kvbytes))
+        return KB_ATTN_ERR_ALIAS;
+    if (int rc = check_lse(lse, (size_t)n_q_heads * q_rows, {{q, qbytes}, {k, kvbytes}, {v, kvbytes}, {o, qbytes}}))
+        return rc;
+    if (int rc = check_device({q, k, v, o})) return rc;
+    return launch_prefill_varlen(q, k, v, o, lse, seqs, q_rows, kv_rows, n_kv_heads, scale, stream);
 }
 
 int kb_attn_partitioned_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, const int64_t* cu_q,
@@ -980,7 +1003,7 @@ int kb_attn_partitioned_varlen(const void* q, const void* k_cache, const void* v
         ranges_overlap(o, qbytes, v_cache, kvbytes))
         return KB_ATTN_ERR_ALIAS;
     if (int rc = check_device({q, k_cache, v_cache, o})) return rc;
-    return launch_prefill_varlen(q, k_cache, v_cache, o, seqs, q_rows, kv_rows, n_kv_heads, scale, stream);
+    return launch_prefill_varlen(q, k_cache, v_cache, o, nullptr, seqs, q_rows, kv_rows, n_kv_heads, scale, stream);
 }
 
 size_t kb_attn_decode_varlen_workspace_bytes(const int64_t* kv_lens, int64_t batch, int32_t n_q_heads,

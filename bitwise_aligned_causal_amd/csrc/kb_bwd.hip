@@ -163,22 +163,69 @@ struct BwdArgs {
     float scale;  // fp32 scale
 };
 
+// Where one sequence's rows live.  Query head h (0 .. Hq - 1 of the sequence)
+// row i is row h * hstride + q_row0 + i of q, o, dout, dq (and of lse);
+// KV head g key j is row g * hstride + kv_row0 + j of k, v, dk, dv; its
+// D / lse2 entries are at h * ws_hstride + ws_row0 + i.  Dense batches:
+// q_row0 = b Hq S, kv_row0 = b Hkv S, hstride = S, ws_row0 = b Hq S_pad,
+// ws_hstride = S_pad.  Packed ragged batches [H, T, 128]: q_row0 = kv_row0 =
+// the sequence's first packed row, hstride = T, ws_row0 = its first padded
+// row, ws_hstride = T_pad.
+struct BwdSeq {
+    int64_t S;
+    int64_t q_row0, kv_row0, hstride;
+    int64_t ws_row0, ws_hstride;
+};
+
+__device__ __forceinline__ BwdSeq dense_seq(const BwdArgs& a, int b) {
+    const int64_t hq = (int64_t)kGroup * a.n_kv_heads;
+    BwdSeq sq;
+    sq.S = a.seq_len;
+    sq.q_row0 = (int64_t)b * hq * a.seq_len;
+    sq.kv_row0 = (int64_t)b * a.n_kv_heads * a.seq_len;
+    sq.hstride = a.seq_len;
+    sq.ws_row0 = (int64_t)b * hq * a.s_pad;
+    sq.ws_hstride = a.s_pad;
+    return sq;
+}
+
+// Ragged launches: at most kBwdMaxSeqs sequences, each padded to a multiple
+// of 64 rows in the workspace; unit_kv / unit_dq are the prefix sums of the
+// dK/dV and dQ work units (KV heads x 128-key blocks, KV heads x 64-row
+// blocks) of the sequences in this launch.
+constexpr int kBwdMaxSeqs = 64;
+struct BwdTable {
+    int64_t row0[kBwdMaxSeqs];  // first packed row
+    int64_t pad0[kBwdMaxSeqs];  // first padded workspace row
+    int32_t len[kBwdMaxSeqs];
+    int32_t unit_kv[kBwdMaxSeqs + 1];
+    int32_t unit_dq[kBwdMaxSeqs + 1];
+    int32_t n_seqs;
+    int64_t t_rows, t_pad;     // rows per head of the packed tensors and of the padded workspace
+    int64_t p_begin, p_count;  // the launch's sequences' padded rows (consecutive)
+};
+
+__device__ __forceinline__ BwdSeq table_seq(const BwdTable& t, int s) {
+    BwdSeq sq;
+    sq.S = t.len[s];
+    sq.q_row0 = t.row0[s];
+    sq.kv_row0 = t.row0[s];
+    sq.hstride = t.t_rows;
+    sq.ws_row0 = t.pad0[s];
+    sq.ws_hstride = t.t_pad;
+    return sq;
+}
+
 // ---------------------------------------------------------------------------
 // D and lse2 per row: 8 lanes per row, 16 elements per lane in order, then a
-// fixed xor butterfly over the 8 lanes.  Rows i >= seq_len of the padded
-// arrays get 0.
+// fixed xor butterfly over the 8 lanes.  Padding rows (i >= the sequence's
+// length) get 0.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-    const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-    const int part = threadIdx.x & 7;
-    const int64_t n_rows = (int64_t)a.batch * kGroup * a.n_kv_heads * a.s_pad;
-    const bool in_range = row < n_rows;
-    const int64_t bh = in_range ? row / a.s_pad : 0;
-    const int64_t i = in_range ? row % a.s_pad : 0;
-    const bool valid = in_range && i < a.seq_len;
+__device__ __forceinline__ void prep_row(const BwdArgs& a, int64_t src_row, int64_t ws_row, bool valid,
+                                         bool in_range, int part) {
     float acc = 0.0f;
     if (valid) {
-        const int64_t src = (bh * a.seq_len + i) * kHeadDim + 16 * part;
+        const int64_t src = src_row * kHeadDim + 16 * part;
         const u32x4* dp = reinterpret_cast<const u32x4*>(a.dout + src);
         const u32x4* op = reinterpret_cast<const u32x4*>(a.o + src);
 #pragma unroll
@@ -193,9 +240,34 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     acc = acc + __shfl_xor(acc, 2);
     acc = acc + __shfl_xor(acc, 4);
     if (in_range && part == 0) {
-        a.ws_d[row] = valid ? acc : 0.0f;
-        a.ws_lse2[row] = valid ? a.lse[bh * a.seq_len + i] * kLog2e : 0.0f;
+        a.ws_d[ws_row] = valid ? acc : 0.0f;
+        a.ws_lse2[ws_row] = valid ? a.lse[src_row] * kLog2e : 0.0f;
     }
+}
+
+// dense: workspace row w = (b Hq + h) S_pad + i
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int64_t n_rows = (int64_t)a.batch * kGroup * a.n_kv_heads * a.s_pad;
+    const bool in_range = row < n_rows;
+    const int64_t bh = in_range ? row / a.s_pad : 0;
+    const int64_t i = in_range ? row % a.s_pad : 0;
+    prep_row(a, bh * a.seq_len + i, row, in_range && i < a.seq_len, in_range, threadIdx.x & 7);
+}
+
+// ragged: block x covers padded rows p_begin + 32 (x % nb) .. + 31 of query
+// head x / nb, nb = p_count / 32 blocks per head; a block never straddles
+// two sequences (each is padded to a multiple of 64 rows)
+__global__ __launch_bounds__(256) void bwd_prep_varlen_kernel(BwdArgs a, BwdTable t) {
+    const int64_t nb = t.p_count / 32;
+    const int64_t h = blockIdx.x / nb;
+    const int64_t p = t.p_begin + (blockIdx.x % nb) * 32 + (threadIdx.x >> 3);  // padded row
+    int s = 0;
+    while (s + 1 < t.n_seqs && t.pad0[s + 1] <= p) ++s;
+    const int64_t i = p - t.pad0[s];
+    const bool in_range = p < t.pad0[s] + ((t.len[s] + 63) / 64) * 64 && p >= t.pad0[s];
+    prep_row(a, h * t.t_rows + t.row0[s] + i, h * t.t_pad + p, in_range && i < t.len[s], in_range,
+             threadIdx.x & 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -220,13 +292,14 @@ constexpr int kKvStages = 4;
 constexpr int kPBufBytes = 4 * 4096;                  // fp32 P of the 4 key groups
 constexpr int kKvLoadsPerWave = (2 * kQTileBytes / 1024) / kKvWaves + 1;  // 2 tile loads + 1 block of 8 floats
 
-__device__ __forceinline__ void kv_stage(const BwdArgs& a, int64_t bh0, int t, int64_t qlast, char* stage, int w,
-                                         int lane) {
+__device__ __forceinline__ void kv_stage(const BwdArgs& a, const BwdSeq& sq, int g, int t, int64_t qlast,
+                                         char* stage, int w, int lane) {
     const int64_t q0 = qlast - 32 * (t >> 2);
-    const int64_t bh = bh0 + (t & 3);  // (sequence, query head) row block
-    const char* qb = reinterpret_cast<const char*>(a.q + (bh * a.seq_len + q0) * kHeadDim);
-    const char* db = reinterpret_cast<const char*>(a.dout + (bh * a.seq_len + q0) * kHeadDim);
-    const int64_t last = a.seq_len - 1 - q0;  // last valid row, relative to q0
+    const int64_t hh = kGroup * g + (t & 3);  // query head of the item
+    const int64_t qrow = hh * sq.hstride + sq.q_row0 + q0;
+    const char* qb = reinterpret_cast<const char*>(a.q + qrow * kHeadDim);
+    const char* db = reinterpret_cast<const char*>(a.dout + qrow * kHeadDim);
+    const int64_t last = sq.S - 1 - q0;  // last valid row, relative to q0
     // instructions 0..7 fill Q rows 4i..4i+3, 8..15 fill dO; wave w issues w and w + 8
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -238,13 +311,15 @@ __device__ __forceinline__ void kv_stage(const BwdArgs& a, int64_t bh0, int t, i
     }
     // lse2 / D of the 32 rows (padded arrays, in bounds): wave w moves 8
     // floats with lanes 0..1 (w < 4: lse2[8w ..], else D[8(w-4) ..])
-    const float* src = (w < 4 ? a.ws_lse2 : a.ws_d) + bh * a.s_pad + q0 + 8 * (w & 3);
+    const float* src = (w < 4 ? a.ws_lse2 : a.ws_d) + hh * sq.ws_hstride + sq.ws_row0 + q0 + 8 * (w & 3);
     if (lane < 2) dma16(reinterpret_cast<const char*>(src), (uint32_t)(lane * 16), stage + 2 * kQTileBytes + 32 * w);
 }
 
 // Everything a dK/dV wave needs once its work item is known.
 struct KvWork {
-    int64_t S, K0, k0, bh0, qlast;
+    BwdSeq sq;
+    int g;
+    int64_t S, K0, k0, qlast;
     int n_items, kg, w, lane;
     char* smem;
     char* pbuf;
@@ -328,7 +403,7 @@ __device__ __forceinline__ void kv_loop(const BwdArgs& a, const KvWork& wk, cons
             wait_vm<0>();
         __syncthreads();
         if (t + 2 < wk.n_items)
-            kv_stage(a, wk.bh0, t + 2, wk.qlast, wk.smem + ((t + 2) % kKvStages) * kKvStageBytes, wk.w, lane);
+            kv_stage(a, wk.sq, wk.g, t + 2, wk.qlast, wk.smem + ((t + 2) % kKvStages) * kKvStageBytes, wk.w, lane);
 
         const int it = kP ? t : t - 1;
         if (it < 0 || it >= wk.n_items) continue;
@@ -350,14 +425,63 @@ __device__ __forceinline__ void kv_loop(const BwdArgs& a, const KvWork& wk, cons
     }
 }
 
-__global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + 2 * kPBufBytes];
+// One dK/dV workgroup: keys [128 kb, 128 kb + 128) of KV head g of one sequence.
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, const BwdSeq& sq, int g, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = w & 3;
     const bool pwave = w < 4;
     const int j = lane & 31, h = lane >> 5;
+    KvWork wk;
+    wk.sq = sq;
+    wk.g = g;
+    wk.S = sq.S;
+    wk.K0 = (int64_t)kb * kKvKeys;
+    wk.k0 = wk.K0 + 32 * kg;  // this wave's first key
+    // query tiles from the last one down to K0: every block of a (sequence,
+    // KV head) starts at the same rows, so the blocks running together on an
+    // XCD read the same Q / dO rows at about the same time (one L2 fetch)
+    wk.qlast = ((wk.S - 1) >> 5) << 5;
+    wk.n_items = 4 * (int)((wk.qlast - wk.K0) / 32 + 1);
+    wk.kg = kg;
+    wk.w = w;
+    wk.lane = lane;
+    wk.smem = smem;
+    wk.pbuf = smem + kKvStages * kKvStageBytes;
+    const int64_t S = wk.S;
 
+    kv_stage(a, sq, g, 0, wk.qlast, smem, w, lane);
+    if (wk.n_items >= 2) kv_stage(a, sq, g, 1, wk.qlast, smem + kKvStageBytes, w, lane);
+
+    // this wave's K (P-wave) or V (dS-wave) rows as B operands: lane (key j,
+    // half h) holds row k0 + j, d = 16 st + 8h .. + 7 (rows beyond S read row S - 1)
+    const int64_t kv0 = (int64_t)g * sq.hstride + sq.kv_row0;  // row of key 0
+    bf16x8 kvf[8];
+    {
+        int64_t key = wk.k0 + j;
+        key = key < S ? key : S - 1;
+        const uint16_t* src = (pwave ? a.k : a.v) + (kv0 + key) * kHeadDim;
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+            kvf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * st + 8 * h));
+    }
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = zero16();
+    const int64_t row = (kv0 + wk.k0 + j) * kHeadDim;
+    if (pwave) {
+        kv_loop<true>(a, wk, kvf, acc);
+        if (wk.k0 + j < S) store_col(a.dv + row, acc, 1.0f, h);
+    } else {
+        kv_loop<false>(a, wk, kvf, acc);
+        if (wk.k0 + j < S) store_col(a.dk + row, acc, a.scale, h);
+    }
+}
+
+// Dense batch: [B, H, S, 128].
+__global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + 2 * kPBufBytes];
     const int n_kb = (int)((a.seq_len + kKvKeys - 1) / kKvKeys);
     const int nbg = a.batch * a.n_kv_heads;
     const int x = blockIdx.x;
@@ -372,50 +496,18 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
         bg = x % nbg;
         kb = x / nbg;
     }
-    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
-    KvWork wk;
-    wk.S = a.seq_len;
-    wk.K0 = (int64_t)kb * kKvKeys;
-    wk.k0 = wk.K0 + 32 * kg;  // this wave's first key
-    wk.bh0 = (int64_t)b * kGroup * a.n_kv_heads + kGroup * g;
-    // query tiles from the last one down to K0: every block of a (sequence,
-    // KV head) starts at the same rows, so the blocks running together on an
-    // XCD read the same Q / dO rows at about the same time (one L2 fetch)
-    wk.qlast = ((wk.S - 1) >> 5) << 5;
-    wk.n_items = 4 * (int)((wk.qlast - wk.K0) / 32 + 1);
-    wk.kg = kg;
-    wk.w = w;
-    wk.lane = lane;
-    wk.smem = smem;
-    wk.pbuf = smem + kKvStages * kKvStageBytes;
-    const int64_t S = wk.S;
+    dkdv_body(a, dense_seq(a, bg / a.n_kv_heads), bg % a.n_kv_heads, kb, smem);
+}
 
-    kv_stage(a, wk.bh0, 0, wk.qlast, smem, w, lane);
-    if (wk.n_items >= 2) kv_stage(a, wk.bh0, 1, wk.qlast, smem + kKvStageBytes, w, lane);
-
-    // this wave's K (P-wave) or V (dS-wave) rows as B operands: lane (key j,
-    // half h) holds row k0 + j, d = 16 st + 8h .. + 7 (rows beyond S read row S - 1)
-    bf16x8 kvf[8];
-    {
-        int64_t key = wk.k0 + j;
-        key = key < S ? key : S - 1;
-        const uint16_t* src = (pwave ? a.k : a.v) + ((int64_t)bg * S + key) * kHeadDim;
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-            kvf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * st + 8 * h));
-    }
-
-    f32x16 acc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] = zero16();
-    const int64_t row = ((int64_t)bg * S + wk.k0 + j) * kHeadDim;
-    if (pwave) {
-        kv_loop<true>(a, wk, kvf, acc);
-        if (wk.k0 + j < S) store_col(a.dv + row, acc, 1.0f, h);
-    } else {
-        kv_loop<false>(a, wk, kvf, acc);
-        if (wk.k0 + j < S) store_col(a.dk + row, acc, a.scale, h);
-    }
+// Ragged batch (packed [H, T, 128]): units of a sequence are (128-key block,
+// KV head), longest blocks first.
+__global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_varlen_kernel(BwdArgs a, BwdTable t) {
+    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + 2 * kPBufBytes];
+    const int x = blockIdx.x;
+    int s = 0;
+    while (s + 1 < t.n_seqs && t.unit_kv[s + 1] <= x) ++s;
+    const int u = x - t.unit_kv[s];
+    dkdv_body(a, table_seq(t, s), u % a.n_kv_heads, u / a.n_kv_heads, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -434,32 +526,21 @@ __device__ __forceinline__ void dq_stage(const uint16_t* kb, const uint16_t* vb,
     stage_rows<false>(vb, key0, last, stage + kKBytes, w, kDqWaves, lane);
 }
 
-__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kTileBytes];
+// One dQ workgroup: positions [64 pb, 64 pb + 64) of the 4 query heads of KV
+// head g of one sequence.
+__device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int g, int pb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31, h = lane >> 5;
 
-    const int64_t S = a.seq_len;
-    const int n_pb = (int)((S + 63) / 64);
-    const int nbg = a.batch * a.n_kv_heads;
-    const int x = blockIdx.x;
-    int bg, pbr;
-    if ((nbg & 7) == 0) {
-        const int i = x >> 3;
-        bg = (i / n_pb) * 8 + (x & 7);
-        pbr = i % n_pb;
-    } else {
-        bg = x % nbg;
-        pbr = x / nbg;
-    }
-    const int pb = n_pb - 1 - pbr;  // longest rows first
-    const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
-    const int64_t bh = (int64_t)b * kGroup * a.n_kv_heads + kGroup * g + (w & 3);
+    const int64_t S = sq.S;
+    const int64_t hh = kGroup * g + (w & 3);  // this wave's query head
     const int64_t pos = (int64_t)pb * 64 + 32 * (w >> 2) + j;
     const bool active = pos < S;
-    const uint16_t* kbase = a.k + (int64_t)bg * S * kHeadDim;
-    const uint16_t* vbase = a.v + (int64_t)bg * S * kHeadDim;
+    const int64_t qrow0 = hh * sq.hstride + sq.q_row0;  // row of position 0 of this head
+    const int64_t wsrow0 = hh * sq.ws_hstride + sq.ws_row0;
+    const uint16_t* kbase = a.k + ((int64_t)g * sq.hstride + sq.kv_row0) * kHeadDim;
+    const uint16_t* vbase = a.v + ((int64_t)g * sq.hstride + sq.kv_row0) * kHeadDim;
     const int t_last = pb;
 
     dq_stage(kbase, vbase, 0, S - 1, smem, w, lane);
@@ -470,7 +551,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
     float lse2 = 0.0f, Di = 0.0f;
     {
         const int64_t r = active ? pos : S - 1;
-        const int64_t qrow = (bh * S + r) * kHeadDim;
+        const int64_t qrow = (qrow0 + r) * kHeadDim;
         const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
@@ -480,8 +561,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
             df[st] = __builtin_bit_cast(bf16x8, active ? y4 : zero);
         }
         if (active) {
-            lse2 = a.ws_lse2[bh * a.s_pad + pos];
-            Di = a.ws_d[bh * a.s_pad + pos];
+            lse2 = a.ws_lse2[wsrow0 + pos];
+            Di = a.ws_d[wsrow0 + pos];
         }
     }
 
@@ -547,7 +628,38 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
         }
     }
 
-    if (active) store_col(a.dq + (bh * S + pos) * kHeadDim, acc, a.scale, h);
+    if (active) store_col(a.dq + (qrow0 + pos) * kHeadDim, acc, a.scale, h);
+}
+
+// Dense batch: [B, H, S, 128].
+__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kTileBytes];
+    const int n_pb = (int)((a.seq_len + 63) / 64);
+    const int nbg = a.batch * a.n_kv_heads;
+    const int x = blockIdx.x;
+    int bg, pbr;
+    if ((nbg & 7) == 0) {
+        const int i = x >> 3;
+        bg = (i / n_pb) * 8 + (x & 7);
+        pbr = i % n_pb;
+    } else {
+        bg = x % nbg;
+        pbr = x / nbg;
+    }
+    // longest rows first
+    dq_body(a, dense_seq(a, bg / a.n_kv_heads), bg % a.n_kv_heads, n_pb - 1 - pbr, smem);
+}
+
+// Ragged batch (packed [H, T, 128]): units of a sequence are (64-row block,
+// KV head), longest blocks first.
+__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_varlen_kernel(BwdArgs a, BwdTable t) {
+    __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kTileBytes];
+    const int x = blockIdx.x;
+    int s = 0;
+    while (s + 1 < t.n_seqs && t.unit_dq[s + 1] <= x) ++s;
+    const int u = x - t.unit_dq[s];
+    const int n_pb = (t.len[s] + 63) / 64;
+    dq_body(a, table_seq(t, s), u % a.n_kv_heads, n_pb - 1 - u / a.n_kv_heads, smem);
 }
 
 }  // namespace bwd
@@ -584,6 +696,23 @@ int on_device(std::initializer_list<const void*> ptrs) {
 }
 
 int64_t padded_rows(int64_t seq_len) { return (seq_len + 63) / 64 * 64; }
+
+// Checks a ragged batch's host offsets (batch + 1 entries, from >= 0,
+// non-decreasing, each sequence at most kMaxSeq rows) and returns the packed
+// row count and the padded workspace rows (each sequence padded to 64).
+int ragged_rows(const int64_t* cu, int64_t batch, int64_t* t_rows, int64_t* t_pad) {
+    if (cu[0] < 0) return KB_ATTN_ERR_LENGTH;
+    int64_t pad = 0;
+    for (int64_t i = 0; i < batch; ++i) {
+        const int64_t len = cu[i + 1] - cu[i];
+        if (len < 0 || len > kMaxSeq) return KB_ATTN_ERR_LENGTH;
+        pad += padded_rows(len);
+    }
+    if (cu[batch] > (kMaxSeq << 6) || pad > (kMaxSeq << 6)) return KB_ATTN_ERR_LENGTH;
+    if (t_rows) *t_rows = cu[batch];
+    if (t_pad) *t_pad = pad;
+    return KB_ATTN_OK;
+}
 
 }  // namespace
 
@@ -654,6 +783,107 @@ int kb_attn_backward(const void* q, const void* k, const void* v, const void* o,
     if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)dq_grid), dim3(64 * kDqWaves), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+    return KB_ATTN_OK;
+}
+
+size_t kb_attn_backward_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t batch, int32_t n_q_heads,
+                                               int32_t head_dim) {
+    if (!cu_seqlens || batch < 1 || n_q_heads < 1 || head_dim != kHeadDim) return 0;
+    int64_t t_pad = 0;
+    if (ragged_rows(cu_seqlens, batch, nullptr, &t_pad) != KB_ATTN_OK) return 0;
+    return (size_t)2 * n_q_heads * t_pad * sizeof(float);
+}
+
+int kb_attn_backward_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, const int64_t* cu_seqlens, int64_t batch,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens || batch < 1)
+        return KB_ATTN_ERR_INVALID_ARG;
+    if (n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return KB_ATTN_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim || n_q_heads != kGroup * n_kv_heads) return KB_ATTN_ERR_UNSUPPORTED;
+    if (!(scale > 0.0f) || !(scale < __builtin_inff())) return KB_ATTN_ERR_INVALID_ARG;
+    int64_t t_rows = 0, t_pad = 0;
+    if (int rc = ragged_rows(cu_seqlens, batch, &t_rows, &t_pad)) return rc;
+    const size_t need = (size_t)2 * n_q_heads * t_pad * sizeof(float);
+    if (need && (!workspace || workspace_bytes < need)) return KB_ATTN_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+        if ((uintptr_t)p & 15u) return KB_ATTN_ERR_ALIGNMENT;
+    if (need && ((uintptr_t)workspace & 15u)) return KB_ATTN_ERR_ALIGNMENT;
+    if ((uintptr_t)lse & 3u) return KB_ATTN_ERR_ALIGNMENT;
+    const size_t qb = (size_t)n_q_heads * t_rows * kHeadDim * 2;
+    const size_t kb_ = (size_t)n_kv_heads * t_rows * kHeadDim * 2;
+    const size_t lb = (size_t)n_q_heads * t_rows * sizeof(float);
+    const std::pair<const void*, size_t> outs[] = {{dq, qb}, {dk, kb_}, {dv, kb_}, {need ? workspace : nullptr, need}};
+    const std::pair<const void*, size_t> ins[] = {{q, qb}, {k, kb_}, {v, kb_}, {o, qb}, {dout, qb}, {lse, lb}};
+    for (size_t i = 0; i < 4; ++i) {
+        for (size_t m = i + 1; m < 4; ++m)
+            if (overlap(outs[i].first, outs[i].second, outs[m].first, outs[m].second)) return KB_ATTN_ERR_ALIAS;
+        for (const auto& in : ins)
+            if (overlap(outs[i].first, outs[i].second, in.first, in.second)) return KB_ATTN_ERR_ALIAS;
+    }
+    if (int rc = on_device({q, k, v, o, dout, lse, dq, dk, dv})) return rc;
+    if (need)
+        if (int rc = on_device({workspace})) return rc;
+    if (t_rows == 0) return KB_ATTN_OK;  // every sequence is empty
+
+    BwdArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.o = (const uint16_t*)o;
+    a.dout = (const uint16_t*)dout;
+    a.lse = lse;
+    a.dq = (uint16_t*)dq;
+    a.dk = (uint16_t*)dk;
+    a.dv = (uint16_t*)dv;
+    a.seq_len = 0;  // per sequence, from the table
+    a.s_pad = 0;
+    a.ws_d = (float*)workspace;
+    a.ws_lse2 = (float*)workspace + (int64_t)n_q_heads * t_pad;
+    a.batch = 0;
+    a.n_kv_heads = n_kv_heads;
+    a.c = (float)((double)scale * 1.4426950408889634073599246810019);
+    a.scale = scale;
+
+    // sequences in the caller's order, at most kBwdMaxSeqs non-empty ones per
+    // launch (a sequence's bits do not depend on which launch carries it)
+    int64_t pad = 0;
+    int64_t i = 0;
+    while (i < batch) {
+        BwdTable t;
+        t.n_seqs = 0;
+        t.t_rows = t_rows;
+        t.t_pad = t_pad;
+        t.p_begin = pad;
+        int64_t units_kv = 0, units_dq = 0;
+        for (; i < batch && t.n_seqs < kBwdMaxSeqs; ++i) {
+            const int64_t len = cu_seqlens[i + 1] - cu_seqlens[i];
+            if (len == 0) continue;
+            const int n = t.n_seqs++;
+            t.row0[n] = cu_seqlens[i];
+            t.pad0[n] = pad;
+            t.len[n] = (int32_t)len;
+            t.unit_kv[n] = (int32_t)units_kv;
+            t.unit_dq[n] = (int32_t)units_dq;
+            units_kv += (int64_t)n_kv_heads * ((len + kKvKeys - 1) / kKvKeys);
+            units_dq += (int64_t)n_kv_heads * ((len + 63) / 64);
+            pad += padded_rows(len);
+            if (units_kv > INT32_MAX || units_dq > INT32_MAX) return KB_ATTN_ERR_LENGTH;
+        }
+        if (t.n_seqs == 0) break;
+        t.unit_kv[t.n_seqs] = (int32_t)units_kv;
+        t.unit_dq[t.n_seqs] = (int32_t)units_dq;
+        t.p_count = pad - t.p_begin;
+        const int64_t prep_grid = (int64_t)n_q_heads * (t.p_count / 32);
+        if (prep_grid > INT32_MAX) return KB_ATTN_ERR_LENGTH;
+        hipLaunchKernelGGL(bwd_prep_varlen_kernel, dim3((unsigned)prep_grid), dim3(256), 0, stream, a, t);
+        if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+        hipLaunchKernelGGL(bwd_dkdv_varlen_kernel, dim3((unsigned)units_kv), dim3(64 * kKvWaves), 0, stream, a, t);
+        if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+        hipLaunchKernelGGL(bwd_dq_varlen_kernel, dim3((unsigned)units_dq), dim3(64 * kDqWaves), 0, stream, a, t);
+        if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
+    }
     return KB_ATTN_OK;
 }
 

@@ -239,6 +239,44 @@ int kb_attn_backward(const void* q, const void* k, const void* v, const void* o,
 size_t kb_attn_backward_workspace_bytes(int64_t batch, int64_t seq_len, int32_t n_q_heads,
                                         int32_t head_dim);
 
+/*
+ * Ragged batches for training (README "Background": the rollout batches the
+ * forward serves are ragged, and the policy update runs on the same
+ * sequences), in the packed head-major layout of the ragged forward calls:
+ *   kb_attn_prefill_varlen_lse   kb_attn_prefill_varlen plus lse fp32
+ *                                [n_q_heads, cu_seqlens[batch]] (DEVICE,
+ *                                4-byte aligned, overlapping nothing else);
+ *                                each row's lse bits equal those of the dense
+ *                                prefill_lse of its sequence alone
+ *   kb_attn_backward_varlen      kb_attn_backward for every sequence of the
+ *                                batch: q, o, dout, dq [n_q_heads, T, 128],
+ *                                k, v, dk, dv [n_kv_heads, T, 128], lse
+ *                                [n_q_heads, T], T = cu_seqlens[batch];
+ *                                sequence i is rows cu_seqlens[i] ..
+ *                                cu_seqlens[i+1] - 1 of every head (full
+ *                                causal, positions 0 .. len - 1); its
+ *                                gradient bits equal those of the dense
+ *                                backward of that sequence alone
+ * cu_seqlens is a HOST array of batch + 1 non-decreasing offsets from >= 0
+ * (each sequence at most 2^30 rows, else KB_ATTN_ERR_LENGTH), read during the
+ * call and not kept; empty sequences are skipped.  The backward's workspace
+ * (DEVICE, 16-byte aligned; NULL when its size is 0) holds each sequence's
+ * rows padded to a multiple of 64.  Other rules as for the dense calls.
+ */
+int kb_attn_prefill_varlen_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int64_t* cu_seqlens, int64_t batch, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, float scale, hipStream_t stream);
+int kb_attn_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            const int64_t* cu_seqlens, int64_t batch, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, float scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes kb_attn_backward_varlen needs for these host offsets (0
+ * when every sequence is empty or the offsets are invalid). */
+size_t kb_attn_backward_varlen_workspace_bytes(const int64_t* cu_seqlens, int64_t batch,
+                                               int32_t n_q_heads, int32_t head_dim);
+
 /* Static description of an error code (never NULL). */
 const char* kb_attn_strerror(int code);
 

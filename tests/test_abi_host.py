@@ -202,3 +202,40 @@ def test_backward_workspace_bytes():
 ])
 def test_backward_rejected_before_launch(kw, expect):
     assert backward(**kw) == expect
+
+
+def backward_varlen(cu=(0, 100, 164, 300), **kw):
+    a = dict(q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, hq=32, hkv=8, d=128, scale=SCALE, ws=W,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    arr = (ctypes.c_int64 * len(cu))(*cu)
+    return kb.lib().kb_attn_backward_varlen(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                                            a["dv"], arr, len(cu) - 1, a["hq"], a["hkv"], a["d"], a["scale"], a["ws"],
+                                            a["ws_bytes"], None)
+
+
+def test_backward_varlen_workspace_bytes():
+    # each sequence padded to a multiple of 64 rows: 128 + 64 + 192 = 384
+    assert kb.backward_varlen_workspace_bytes([0, 100, 164, 300]) == 2 * 32 * 384 * 4
+    assert kb.backward_varlen_workspace_bytes([0, 0, 0]) == 0
+    assert kb.backward_varlen_workspace_bytes([0, 5, 3]) == 0  # decreasing offsets
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(dv=None), INVALID), (dict(scale=0.0), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(hq=16), UNSUPPORTED),
+    (dict(cu=(0, 10, 5)), LENGTH), (dict(cu=(-1, 10)), LENGTH), (dict(cu=(0, (1 << 30) + 1)), LENGTH),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=2 * 32 * 384 * 4 - 1), WORKSPACE),
+    (dict(dq=ctypes.c_void_p(DQ.value + 8)), ALIGN), (dict(lse=ctypes.c_void_p(L.value + 1)), ALIGN),
+    (dict(dq=Q), ALIAS), (dict(dv=DK), ALIAS), (dict(ws=ctypes.c_void_p(DO.value + 64)), ALIAS),
+])
+def test_backward_varlen_rejected_before_launch(kw, expect):
+    assert backward_varlen(**kw) == expect
+
+
+def test_prefill_varlen_lse_rejected_before_launch():
+    cu = (ctypes.c_int64 * 3)(0, 10, 30)
+    f = kb.lib().kb_attn_prefill_varlen_lse
+    assert f(Q, K, V, O, None, cu, 2, 32, 8, 128, SCALE, None) == INVALID
+    assert f(Q, K, V, O, ctypes.c_void_p(L.value + 2), cu, 2, 32, 8, 128, SCALE, None) == ALIGN
+    assert f(Q, K, V, O, ctypes.c_void_p(O.value + 64), cu, 2, 32, 8, 128, SCALE, None) == ALIAS
