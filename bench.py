@@ -101,19 +101,24 @@ def cpu_baseline(q, k, v, target_s: float):
         r = rng.integers(0, S, n)
         return (b * HQ + h) * S + r, r
 
-    rows, pos = sample(max(threads, 32))
-    t0 = time.perf_counter()
-    oracle.attention(q, k, v, rows=rows, threads=threads)
-    dt = time.perf_counter() - t0
-    rate = oracle.row_flops(pos) / max(dt, 1e-6)
-    n = int(max(threads, min(200000, target_s * rate / (4 * D * (S / 2)))))
-    rows, pos = sample(n)
-    t0 = time.perf_counter()
-    ref = oracle.attention(q, k, v, rows=rows, threads=threads)
-    dt = time.perf_counter() - t0
-    flops = oracle.row_flops(pos)
+    # batches of random rows until about target_s seconds of oracle work have
+    # run, each batch sized from the rate measured so far
+    all_rows, refs = [], []
+    flops, dt, n = 0, 0.0, 4 * threads
+    while dt < target_s:
+        rows, pos = sample(n)
+        t0 = time.perf_counter()
+        refs.append(oracle.attention(q, k, v, rows=rows, threads=threads))
+        dt += time.perf_counter() - t0
+        flops += oracle.row_flops(pos)
+        all_rows.append(rows)
+        rate = flops / max(dt, 1e-6)
+        left = target_s - dt
+        n = int(min(200000, max(threads, 0.5 * left * rate / (4 * D * (S / 2)) + threads)))
+    rows = np.concatenate(all_rows)
+    ref = np.concatenate(refs)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} random prefill rows of the same B=16 S=16384 input (fp64 oracle), "
+            "sample": f"{rows.size} random prefill rows of the same B=16 S=16384 input (fp64 oracle), "
                       f"{flops:.3e} FLOPs in {dt:.2f} s"}, rows, ref
 
 
