@@ -295,73 +295,6 @@ __device__ __forceinline__ void qk_tile(const bf16x8 (&qf)[8], const char* sK, i
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
-// Mask, online-softmax update and P V of one tile whose scores are s0, s1.
-// Mask and online-softmax update of one tile whose scores are s0, s1:
-// updates (mc, l) and returns the O rescale factor a, whether any column of
-// the wave has a != 1, and the bf16 P^T operands pf[kb][u] of the tile's four
-// 16-key steps.
-template <bool kMask>
-__device__ __forceinline__ void sm_tile(f32x16 s0, f32x16 s1, int lane, int64_t key0, int64_t pos, float c,
-                                        float& mc, float& l, float& a, bool& any_grow, bf16x8 (&pf)[2][2]) {
-    const int h = lane >> 5;
-    if (kMask) {
-        const float ninf = -__builtin_inff();
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
-            s0[v] = kk > pos ? ninf : s0[v];
-            s1[v] = kk + 32 > pos ? ninf : s1[v];
-        }
-    }
-    float mt = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mt = max3(mt, s0[v], s1[v]);
-    {
-        float lo, hi;
-        halves(mt, lo, hi);
-        mt = fmaxf(lo, hi);
-    }
-
-    // lazy reference max: keep mc while the tile max stays within kLazyTau
-    const float mtc = mt * c;
-    const bool grow = (mtc - mc) > kLazyTau;
-    const float mcn = grow ? mtc : mc;
-    a = grow ? exp2_hw(mc - mcn) : 1.0f;
-    any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
-    const float nmc = -mcn;
-
-    float part[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const float x0 = kb ? s1[8 * u + e] : s0[8 * u + e];
-                const float x1 = kb ? s1[8 * u + e + 1] : s0[8 * u + e + 1];
-                f32x2 pp;
-                pp[0] = exp2_hw(__builtin_fmaf(x0, c, nmc));
-                pp[1] = exp2_hw(__builtin_fmaf(x1, c, nmc));
-                const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-                pf[kb][u][e] = pb[0];
-                pf[kb][u][e + 1] = pb[1];
-                const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-                acc = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, acc, false);
-            }
-            part[kb][u] = acc;
-        }
-    }
-    // fixed tree: each (kb, u) slot group chains its 4 pairs, then
-    // ((00 + 01) + (10 + 11)) per lane half, then (low half + high half)
-    const float ls_half = (part[0][0] + part[0][1]) + (part[1][0] + part[1][1]);
-    float ls_lo, ls_hi;
-    halves(ls_half, ls_lo, ls_hi);
-    const float ls = ls_lo + ls_hi;
-    l = __builtin_fmaf(l, a, ls);
-    mc = mcn;
-}
-
 // o *= a.  o * 1 == o exactly, so skipping the multiply when no column of
 // the wave moved its reference max leaves every bit as it is.
 template <int NDB>
@@ -372,33 +305,6 @@ __device__ __forceinline__ void rescale_o(f32x16 (&o)[NDB], float a, bool any_gr
 #pragma unroll
             for (int v = 0; v < 16; ++v) o[db][v] = o[db][v] * a;
         }
-    }
-}
-
-// o += P V for one tile, key steps in order (kb, u) = (0,0), (0,1), (1,0), (1,1).
-template <int NDB>
-__device__ __forceinline__ void pv_tile(const bf16x8 (&pf)[2][2], const char* sV, int lane, f32x16 (&o)[NDB],
-                                        int dblk0) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16x8 vf = vt_frag(sV, kb, u, dblk0 + db, lane);
-                o[db] = mfma(vf, pf[kb][u], o[db]);
-            }
-        }
-    }
-    if (NDB == 4) {
-        // schedule: 4 fragments (8 reads) ahead, then 1 MFMA per 2 reads
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-#pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
 }
 
@@ -432,9 +338,9 @@ __device__ __forceinline__ void pv_step(const bf16x8& pf, const char* sV, int kb
 }
 
 // One whole tile; kMask selects the masked form (needed only on a tile that
-// holds keys beyond some column's position).  The arithmetic is that of
-// sm_tile + rescale_o + pv_tile; P is produced one 16-key step at a time so
-// that a step's P V products can run beside the next step's exponentials.
+// holds keys beyond some column's position): scores, mask, the lazy
+// reference-max update, then P one 16-key step at a time (p_step) so that a
+// step's P V products (pv_step) can run beside the next step's exponentials.
 // kFirst marks the first tile of a chunk (mc = -inf, l = 0, o = 0 on entry):
 // its reference max always moves and a = 0, and o * 0 = +0 = o, so the
 // rescale is skipped and the products start from a zero accumulator -- the
