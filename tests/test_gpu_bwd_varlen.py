@@ -79,3 +79,29 @@ def test_ragged_backward_equals_dense_per_sequence():
 def test_ragged_backward_two_launches():
     # 70 non-empty sequences: more than one launch's table
     run_case([1 + (i * 37) % 150 for i in range(70)], seed=900)
+
+
+def test_ragged_backward_other_heads():
+    """Hq = 8, Hkv = 2: each sequence's ragged bits equal the dense call's."""
+    m = kb()
+    hq, hkv = 8, 2
+    lens = [77, 1, 200, 64]
+    seqs = []
+    for i, L in enumerate(lens):
+        seqs.append(tuple(kb_gen.normal_bf16(700 + i, t, (1, hq if t in (1, 4) else hkv, L, D)) for t in (1, 2, 3, 4)))
+    cat = [np.ascontiguousarray(np.concatenate([s[t][0] for s in seqs], axis=1)) for t in range(4)]
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    Q, K, V, DO = (dev(x) for x in cat)
+    note("ragged backward Hq=8 Hkv=2")
+    o, lse = m.prefill_varlen_lse(Q, K, V, cu, scale=0.1)
+    dq, dk, dv = m.backward_varlen(Q, K, V, o, DO, lse, cu, scale=0.1)
+    got = [bits(x) for x in (dq, dk, dv)]
+    for i, (q, k, v, do) in enumerate(seqs):
+        a, b = cu[i], cu[i + 1]
+        qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+        od, ld = m.prefill_lse(qd, kd, vd, scale=0.1)
+        ref = [bits(x) for x in m.backward(qd, kd, vd, od, dod, ld, scale=0.1)]
+        for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+            assert np.array_equal(g[:, a:b], r[0]), f"{name} of sequence {i}"
