@@ -9,7 +9,8 @@
 // on the inputs:
 //
 //   bwd_prep_kernel  D_i = <dO_i, O_i> and lse2_i = lse_i * log2(e) per row
-//   bwd_dkdv_kernel  two waves per 32 keys of a KV head; the Q / dO rows of
+//   bwd_dkdv_kernel  two waves per 32 keys of a KV head (192 keys, 12 waves
+//                    per workgroup); the Q / dO rows of
 //                    the 4 query heads stream through LDS in 32-row tiles:
 //                      S    = Q K^T           (A = Q rows,  B = K rows in registers)
 //                      P    = exp2(S c - lse2),  dV^T += dO^T P        (first wave)
@@ -271,26 +272,28 @@ __global__ __launch_bounds__(256) void bwd_prep_varlen_kernel(BwdArgs a, BwdTabl
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 8 waves on 128 keys [K0, K0 + 128) of one (sequence,
-// KV head).  Key group kg = w & 3 covers keys k0 = K0 + 32 kg .. + 31 and is
+// dK, dV: workgroup = 12 waves on 192 keys [K0, K0 + 192) of one (sequence,
+// KV head).  Key group kg = w % 6 covers keys k0 = K0 + 32 kg .. + 31 and is
 // served by two waves:
-//   P-wave  (w < 4)   S = Q K^T, P = exp2(S c - lse2), P to LDS, dV^T += dO^T P
-//   dS-wave (w >= 4)  one item later: dP = dO V^T, P from LDS,
+//   P-wave  (w < 6)   S = Q K^T, P = exp2(S c - lse2), P to LDS, dV^T += dO^T P
+//   dS-wave (w >= 6)  one item later: dP = dO V^T, P from LDS,
 //                     dS = P (dP - D), dK^T += Q^T dS
-// so each wave holds one accumulator set (64 registers) and one of K, V.
+// so each wave holds one accumulator set (64 registers) and one of K, V, and
+// fits in the 168 registers that let three waves share a SIMD.
 // Work items t = 0, 1, ...: query tile q0 = qlast - 32 (t / 4) of query head
 // 4g + (t % 4), from the last tile qlast down to K0.  A 4-stage LDS ring holds
 // each item's Q rows, dO rows (dual swizzle) and its 32 lse2 and 32 D values,
 // loaded two items ahead; P goes through a double buffer.  dK^T and dV^T
 // accumulate over the items in that fixed order.
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 8;
-constexpr int kKvKeys = 128;
+constexpr int kKvWaves = 12;
+constexpr int kKvGroups = 6;
+constexpr int kKvKeys = 32 * kKvGroups;
 constexpr int kQTileBytes = 32 * 256;
 constexpr int kKvStageBytes = 2 * kQTileBytes + 256;  // Q, dO, lse2[32], D[32]
 constexpr int kKvStages = 4;
-constexpr int kPBufBytes = 4 * 4096;                  // fp32 P of the 4 key groups
-constexpr int kKvLoadsPerWave = (2 * kQTileBytes / 1024) / kKvWaves + 1;  // 2 tile loads + 1 block of 8 floats
+constexpr int kPBufBytes = kKvGroups * 4096;          // fp32 P of the key groups
+constexpr int kKvLoadsPerWave = 3;  // waves 0..7: 2 tile loads + 1 block of 8 floats; waves 8..11: none
 
 __device__ __forceinline__ void kv_stage(const BwdArgs& a, const BwdSeq& sq, int g, int t, int64_t qlast,
                                          char* stage, int w, int lane) {
@@ -300,7 +303,9 @@ __device__ __forceinline__ void kv_stage(const BwdArgs& a, const BwdSeq& sq, int
     const char* qb = reinterpret_cast<const char*>(a.q + qrow * kHeadDim);
     const char* db = reinterpret_cast<const char*>(a.dout + qrow * kHeadDim);
     const int64_t last = sq.S - 1 - q0;  // last valid row, relative to q0
-    // instructions 0..7 fill Q rows 4i..4i+3, 8..15 fill dO; wave w issues w and w + 8
+    // waves 0..7 issue the stage's loads (waves 8..11 none): instructions 0..7
+    // fill Q rows 4i..4i+3, 8..15 fill dO; wave w issues w and w + 8
+    if (w >= 8) return;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int i = w + 8 * k;
@@ -429,8 +434,8 @@ __device__ __forceinline__ void kv_loop(const BwdArgs& a, const KvWork& wk, cons
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a, const BwdSeq& sq, int g, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kg = w & 3;
-    const bool pwave = w < 4;
+    const int kg = w % kKvGroups;
+    const bool pwave = w < kKvGroups;
     const int j = lane & 31, h = lane >> 5;
     KvWork wk;
     wk.sq = sq;
