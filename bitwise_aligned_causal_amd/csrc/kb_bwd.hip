@@ -192,7 +192,7 @@ __device__ __forceinline__ BwdSeq dense_seq(const BwdArgs& a, int b) {
 
 // Ragged launches: at most kBwdMaxSeqs sequences, each padded to a multiple
 // of 64 rows in the workspace; unit_kv / unit_dq are the prefix sums of the
-// dK/dV and dQ work units (KV heads x 128-key blocks, KV heads x 64-row
+// dK/dV and dQ work units (KV heads x 192-key blocks, KV heads x 64-row
 // blocks) of the sequences in this launch.
 constexpr int kBwdMaxSeqs = 64;
 struct BwdTable {
@@ -430,7 +430,7 @@ __device__ __forceinline__ void kv_loop(const BwdArgs& a, const KvWork& wk, cons
     }
 }
 
-// One dK/dV workgroup: keys [128 kb, 128 kb + 128) of KV head g of one sequence.
+// One dK/dV workgroup: keys [192 kb, 192 kb + 192) of KV head g of one sequence.
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a, const BwdSeq& sq, int g, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -504,7 +504,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     dkdv_body(a, dense_seq(a, bg / a.n_kv_heads), bg % a.n_kv_heads, kb, smem);
 }
 
-// Ragged batch (packed [H, T, 128]): units of a sequence are (128-key block,
+// Ragged batch (packed [H, T, 128]): units of a sequence are (192-key block,
 // KV head), longest blocks first.
 __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_varlen_kernel(BwdArgs a, BwdTable t) {
     __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + 2 * kPBufBytes];
