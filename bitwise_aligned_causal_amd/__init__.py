@@ -10,6 +10,7 @@ Entry points (KernelBraid / AReaL-TIK README, "Usage" and "Method"):
   prefill(q, k, v)                          causal full-sequence forward
   partitioned(q, k_cache, v_cache, kv_len)  a chunk of rows against cached KV
   decode(q, k_cache, v_cache, kv_len)       one query token
+  decode_multi(q, k_cache, v_cache, kv_len) the last 1..8 tokens (a short partitioned chunk, split-KV)
   unified_prefill / unified_decode          the README's call shapes
   prefill_varlen / partitioned_varlen / decode_varlen
                                             ragged batches, packed [heads, rows, 128]
@@ -94,6 +95,11 @@ def lib() -> ctypes.CDLL:
         L.kb_attn_backward_varlen.restype = ctypes.c_int
         L.kb_attn_backward_varlen_workspace_bytes.argtypes = [p64, i64, i32, i32]
         L.kb_attn_backward_varlen_workspace_bytes.restype = ctypes.c_size_t
+        L.kb_attn_decode_multi.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, f32, vp,
+                                           ctypes.c_size_t, vp]
+        L.kb_attn_decode_multi.restype = ctypes.c_int
+        L.kb_attn_decode_multi_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+        L.kb_attn_decode_multi_workspace_bytes.restype = ctypes.c_size_t
         L.kb_attn_strerror.argtypes = [ctypes.c_int]
         L.kb_attn_strerror.restype = ctypes.c_char_p
         L.kb_attn_contract.argtypes = [ctypes.POINTER(i32)] * 3
@@ -203,6 +209,35 @@ def decode(q, k_cache, v_cache, kv_len: int | None = None, scale: float | None =
     check(lib().kb_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B, kv_len,
                                k_cache.shape[2], Hq, k_cache.shape[1], D, _scale(scale, D), ws_ptr, ws_bytes,
                                _stream(q)))
+    return out
+
+
+def decode_multi_workspace_bytes(batch: int, n_rows: int, kv_len: int, n_q_heads: int = 32,
+                                 head_dim: int = HEAD_DIM) -> int:
+    return int(lib().kb_attn_decode_multi_workspace_bytes(batch, n_rows, kv_len, n_q_heads, head_dim))
+
+
+def decode_multi(q, k_cache, v_cache, kv_len: int | None = None, scale: float | None = None, out=None,
+                 workspace=None):
+    """Decode of the last n_rows <= 8 tokens: q [B, Hq, n_rows, 128], row r
+    at position kv_len - n_rows + r, against caches [B, Hkv, capacity, 128]."""
+    torch = _torch()
+    for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(n, x)
+    B, Hq, n_rows, D = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shape mismatch")
+    kv_len = k_cache.shape[2] if kv_len is None else int(kv_len)
+    need = decode_multi_workspace_bytes(B, n_rows, kv_len, Hq, D)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out)
+    check(lib().kb_attn_decode_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B, n_rows,
+                                     kv_len, k_cache.shape[2], Hq, k_cache.shape[1], D, _scale(scale, D), ws_ptr,
+                                     ws_bytes, _stream(q)))
     return out
 
 
@@ -503,5 +538,5 @@ def unified_decode(q_last, k, v, H_Q: int, H_KV: int, scale: float | None = None
 __all__ = ["prefill", "partitioned", "decode", "unified_prefill", "unified_decode", "contract",
            "decode_workspace_bytes", "prefill_varlen", "partitioned_varlen", "decode_varlen",
            "decode_varlen_workspace_bytes", "decode_paged", "prefill_lse", "partitioned_lse", "decode_lse",
-           "backward", "backward_workspace_bytes", "prefill_varlen_lse", "backward_varlen",
+           "decode_multi", "decode_multi_workspace_bytes", "backward", "backward_workspace_bytes", "prefill_varlen_lse", "backward_varlen",
            "backward_varlen_workspace_bytes", "attention", "lib", "check", "KBAttnError", "LIB_PATH"]

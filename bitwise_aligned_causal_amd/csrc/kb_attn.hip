@@ -280,13 +280,17 @@ struct DecodeArgs {
     uint16_t* o;
     float* ws_o;   // [batch * n_q_heads * n_chunks][128]
     float* ws_ml;  // [batch * n_q_heads * n_chunks][2]: (max * c, sum)
-    float* lse;    // optional: [batch, Hq] log-sum-exp of each row
+    float* lse;    // optional: [batch, Hq, n_rows] log-sum-exp of each row
     int64_t kv_len, cap;
     int32_t batch, n_kv_heads, n_chunks;
+    int32_t n_rows;  // query rows per head (1 = one-token decode, at most kDecodeMaxRows)
     float c;
 };
 
 constexpr int kDecodeWaves = 4;
+// query rows per head a decode workgroup can carry: 4 heads x 8 rows fill the
+// 32 columns of one MFMA block
+constexpr int kDecodeMaxRows = 8;
 // Two stages (64 KiB of LDS) let two decode workgroups share a CU; measured
 // on B=16, L=8192 this streams faster than one workgroup with a deeper ring.
 constexpr int kDecodeStages = 2;
@@ -305,15 +309,16 @@ __device__ __forceinline__ void wait_tiles_decode(int ahead) {
 
 // Everything a decode workgroup needs once its work item is known.
 struct DecodeWork {
-    const uint16_t* q;  // query head 4g + i at row q_row0 + i * q_hstride
+    const uint16_t* q;  // query head 4g + i, row r at row q_row0 + i * q_hstride + r
     uint16_t* o;        // output rows, same indexing
     float* lse;         // optional log-sum-exp output, same row indexing
     int64_t q_row0, q_hstride;
+    int n_rows;         // query rows per head, at positions kv_len - n_rows .. kv_len - 1
     const uint16_t* kbase;  // key 0 of this (sequence, KV head)
     const uint16_t* vbase;
     int64_t kv_len;
     int chunk, n_chunks;
-    int64_t ws_row0;  // partial of query head 4g + i, this chunk: ws row ws_row0 + i * n_chunks + chunk
+    int64_t ws_row0;  // partial of query head 4g + i, row r, this chunk: ws row ws_row0 + (i n_rows + r) n_chunks + chunk
     // paged caches only: this sequence's row of the block table and the pool
     const int32_t* pages;
     const uint16_t* kpool;
@@ -336,16 +341,22 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk = wk.chunk;
     const int j = lane & 31, h = lane >> 5;
-    const bool active = j < kGroup;
-    const int hi = active ? j : 0;  // query head 4g + hi
+    const int n_rows = wk.n_rows;
+    // MFMA column j = query head 4g + hi, row ri (columns beyond 4 n_rows hold zeros)
+    const bool col = j < kGroup * n_rows;
+    const int hi = col ? j / n_rows : 0;
+    const int ri = col ? j % n_rows : 0;
     const int64_t kv_len = wk.kv_len;
-    const int64_t pos = kv_len - 1;
+    const int64_t pos = kv_len - n_rows + ri;
 
     const uint16_t* kbase = wk.kbase;
     const uint16_t* vbase = wk.vbase;
     const int n_tiles = (int)((kv_len + kTile - 1) / kTile);
     const int t0 = chunk * kTilesPerChunk;
     const int t1 = min(t0 + kTilesPerChunk, n_tiles);
+    // a row takes part in the chunks up to the one holding its position; in a
+    // later chunk every key is masked for it and its column is not stored
+    const bool active = col && pos >= (int64_t)t0 * kTile;
 
     StagePlan<kDecodeWaves> plan;
     stage_plan(plan, lane, w);
@@ -376,7 +387,7 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
         if (t0 + i < t1) stage(t0 + i, smem + i * kTileBytes);
     }
 
-    const int64_t qrow_idx = wk.q_row0 + (int64_t)hi * wk.q_hstride;
+    const int64_t qrow_idx = wk.q_row0 + (int64_t)hi * wk.q_hstride + ri;
     bf16x8 qf[8];
     {
         const uint16_t* qrow = wk.q + qrow_idx * kHeadDim;
@@ -399,8 +410,9 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
         if (t + kDecodeStages - 1 < t1)
             stage(t + kDecodeStages - 1, smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * kTileBytes);
         const char* buf = smem + ((t - t0) % kDecodeStages) * kTileBytes;
-        // only the context's last tile can hold keys beyond kv_len - 1
-        if (t < n_tiles - 1)
+        // a tile needs the mask when it holds keys beyond the first row's
+        // position (only the context's last tile when n_rows = 1)
+        if (t < n_tiles - 1 && (int64_t)t * kTile + kTile - 1 <= kv_len - n_rows)
             tile_step<1, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, w);
         else
             tile_step<1, true>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, w);
@@ -422,7 +434,7 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
         if (wk.lse && w == 0 && h == 0) wk.lse[qrow_idx] = lse_of(mc, l);
         return;
     }
-    const int64_t prow = wk.ws_row0 + (int64_t)hi * wk.n_chunks + chunk;
+    const int64_t prow = wk.ws_row0 + ((int64_t)hi * n_rows + ri) * wk.n_chunks + chunk;
     float* po = ws_o + prow * kHeadDim;
 #pragma unroll
     for (int b4 = 0; b4 < 4; ++b4) {
@@ -451,8 +463,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     wk.q = a.q;
     wk.o = a.o;
     wk.lse = a.lse;
-    wk.q_row0 = (int64_t)b * n_q_heads + kGroup * g;
-    wk.q_hstride = 1;
+    wk.q_row0 = ((int64_t)b * n_q_heads + kGroup * g) * a.n_rows;
+    wk.q_hstride = a.n_rows;
+    wk.n_rows = a.n_rows;
     const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * a.cap * kHeadDim;
     wk.kbase = a.k + kvoff;
     wk.vbase = a.v + kvoff;
@@ -468,7 +481,9 @@ struct CombineArgs {
     const float* ws_ml;
     uint16_t* o;
     float* lse;  // optional: [rows] log-sum-exp
+    int64_t kv_len;
     int32_t n_chunks;
+    int32_t n_rows;  // rows per head: output row R is row R % n_rows of its head
     float c;
 };
 
@@ -498,7 +513,10 @@ __device__ __forceinline__ void combine_row(const float* ws_o, const float* ws_m
 // order, finalize.
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     const int64_t row = blockIdx.x;
-    combine_row(a.ws_o, a.ws_ml, row * a.n_chunks, a.n_chunks, a.o + row * kHeadDim, a.lse ? a.lse + row : nullptr);
+    // the row's chunks: those up to the one holding its position
+    const int64_t pos = a.kv_len - a.n_rows + row % a.n_rows;
+    const int nc = (int)(pos / kChunk) + 1;
+    combine_row(a.ws_o, a.ws_ml, row * a.n_chunks, nc, a.o + row * kHeadDim, a.lse ? a.lse + row : nullptr);
 }
 
 // Ragged decode: one query token per sequence, q, o [Hq, n_seq_total, 128]
@@ -546,6 +564,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_varlen_kernel(Decode
     wk.lse = nullptr;
     wk.q_row0 = (int64_t)t.seq[s] * a.tok_stride + (int64_t)kGroup * g * a.head_stride;
     wk.q_hstride = a.head_stride;
+    wk.n_rows = 1;
     if (kPaged) {
         wk.kbase = wk.vbase = nullptr;
         wk.pages = a.block_table + (int64_t)t.seq[s] * a.max_pages;
@@ -835,17 +854,18 @@ int partitioned_entry(const void* q, const void* k_cache, const void* v_cache, v
 }
 
 int decode_entry(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int64_t batch,
-                 int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                 float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                 int64_t n_rows, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
+                 int32_t head_dim, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!q || !k_cache || !v_cache || !o || batch < 1) return KB_ATTN_ERR_INVALID_ARG;
     if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
     if (int rc = check_scale(scale)) return rc;
-    if (kv_len < 1 || kv_len > kv_capacity) return KB_ATTN_ERR_LENGTH;
+    if (n_rows < 1 || n_rows > kDecodeMaxRows) return KB_ATTN_ERR_UNSUPPORTED;
+    if (kv_len < n_rows || kv_len > kv_capacity) return KB_ATTN_ERR_LENGTH;
     if (kv_capacity > kMaxLen || batch * n_kv_heads > INT32_MAX) return KB_ATTN_ERR_LENGTH;
-    const size_t need = kb_attn_decode_workspace_bytes(batch, kv_len, n_q_heads, head_dim);
+    const size_t need = kb_attn_decode_multi_workspace_bytes(batch, n_rows, kv_len, n_q_heads, head_dim);
     if (need && (!workspace || workspace_bytes < need)) return KB_ATTN_ERR_WORKSPACE;
     if (int rc = check_aligned({q, k_cache, v_cache, o, need ? workspace : nullptr})) return rc;
-    const size_t qbytes = (size_t)batch * n_q_heads * kHeadDim * 2;
+    const size_t qbytes = (size_t)batch * n_q_heads * n_rows * kHeadDim * 2;
     const size_t kvbytes = (size_t)batch * n_kv_heads * kv_capacity * kHeadDim * 2;
     if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k_cache, kvbytes) ||
         ranges_overlap(o, qbytes, v_cache, kvbytes) || (need && ranges_overlap(o, qbytes, workspace, need)))
@@ -853,14 +873,14 @@ int decode_entry(const void* q, const void* k_cache, const void* v_cache, void* 
     if (need && (ranges_overlap(workspace, need, q, qbytes) || ranges_overlap(workspace, need, k_cache, kvbytes) ||
                  ranges_overlap(workspace, need, v_cache, kvbytes)))
         return KB_ATTN_ERR_ALIAS;
-    if (int rc = check_lse(lse, (size_t)batch * n_q_heads,
+    if (int rc = check_lse(lse, (size_t)batch * n_q_heads * n_rows,
                            {{q, qbytes}, {k_cache, kvbytes}, {v_cache, kvbytes}, {o, qbytes},
                             {need ? workspace : nullptr, need}}))
         return rc;
     if (int rc = check_device({q, k_cache, v_cache, o, need ? workspace : nullptr})) return rc;
 
     const int64_t nc = n_chunks_of(kv_len);
-    const int64_t rows = batch * n_q_heads;
+    const int64_t rows = batch * n_q_heads * n_rows;
     DecodeArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k_cache;
@@ -874,6 +894,7 @@ int decode_entry(const void* q, const void* k_cache, const void* v_cache, void* 
     a.batch = (int32_t)batch;
     a.n_kv_heads = n_kv_heads;
     a.n_chunks = (int32_t)nc;
+    a.n_rows = (int32_t)n_rows;
     a.c = contract_c(scale);
     const int64_t grid = batch * n_kv_heads * nc;
     if (grid > INT32_MAX || rows > INT32_MAX) return KB_ATTN_ERR_LENGTH;
@@ -885,7 +906,9 @@ int decode_entry(const void* q, const void* k_cache, const void* v_cache, void* 
         cmb.ws_ml = a.ws_ml;
         cmb.o = a.o;
         cmb.lse = lse;
+        cmb.kv_len = kv_len;
         cmb.n_chunks = (int32_t)nc;
+        cmb.n_rows = (int32_t)n_rows;
         cmb.c = a.c;
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(kHeadDim), 0, stream, cmb);
         if (hipGetLastError() != hipSuccess) return KB_ATTN_ERR_HIP;
@@ -934,16 +957,33 @@ size_t kb_attn_decode_workspace_bytes(int64_t batch, int64_t kv_len, int32_t n_q
 int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch, int64_t kv_len,
                    int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return decode_entry(q, k_cache, v_cache, o, nullptr, batch, kv_len, kv_capacity, n_q_heads, n_kv_heads, head_dim,
-                        scale, workspace, workspace_bytes, stream);
+    return decode_entry(q, k_cache, v_cache, o, nullptr, batch, 1, kv_len, kv_capacity, n_q_heads, n_kv_heads,
+                        head_dim, scale, workspace, workspace_bytes, stream);
 }
 
 int kb_attn_decode_lse(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int64_t batch,
                        int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                        float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!lse) return KB_ATTN_ERR_INVALID_ARG;
-    return decode_entry(q, k_cache, v_cache, o, lse, batch, kv_len, kv_capacity, n_q_heads, n_kv_heads, head_dim,
-                        scale, workspace, workspace_bytes, stream);
+    return decode_entry(q, k_cache, v_cache, o, lse, batch, 1, kv_len, kv_capacity, n_q_heads, n_kv_heads,
+                        head_dim, scale, workspace, workspace_bytes, stream);
+}
+
+size_t kb_attn_decode_multi_workspace_bytes(int64_t batch, int64_t n_rows, int64_t kv_len, int32_t n_q_heads,
+                                            int32_t head_dim) {
+    if (batch < 1 || n_rows < 1 || n_rows > kDecodeMaxRows || kv_len < n_rows || n_q_heads < 1 ||
+        head_dim != kHeadDim || kv_len > kMaxLen)
+        return 0;
+    const int64_t nc = n_chunks_of(kv_len);
+    if (nc == 1) return 0;
+    return (size_t)batch * n_q_heads * n_rows * nc * (kHeadDim + 2) * sizeof(float);
+}
+
+int kb_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch,
+                         int64_t n_rows, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
+                         int32_t head_dim, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_entry(q, k_cache, v_cache, o, nullptr, batch, n_rows, kv_len, kv_capacity, n_q_heads, n_kv_heads,
+                        head_dim, scale, workspace, workspace_bytes, stream);
 }
 
 int kb_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, const int64_t* cu_seqlens,

@@ -109,6 +109,28 @@ size_t kb_attn_decode_workspace_bytes(int64_t batch, int64_t kv_len, int32_t n_q
                                       int32_t head_dim);
 
 /*
+ * Decode of the last n_rows tokens (1 <= n_rows <= 8, else
+ * KB_ATTN_ERR_UNSUPPORTED), e.g. several drafted tokens checked at once: the
+ * partitioned forward of a short chunk ("Method": partitioned forward
+ * execution), run with decode's split over 1024-key chunks.  Row r of each
+ * head sits at position kv_len - n_rows + r (n_rows <= kv_len <= kv_capacity,
+ * else KB_ATTN_ERR_LENGTH), and its bits equal those of the prefill row at
+ * that position (a row takes part only in the chunks up to the one holding
+ * its position).
+ * q, o: [batch, n_q_heads, n_rows, 128]; caches as kb_attn_decode; workspace
+ * as kb_attn_decode, sized by kb_attn_decode_multi_workspace_bytes.
+ */
+int kb_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache, void* o,
+                         int64_t batch, int64_t n_rows, int64_t kv_len, int64_t kv_capacity,
+                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes kb_attn_decode_multi needs (0 when kv_len fits in one
+ * chunk; 0 for invalid sizes). */
+size_t kb_attn_decode_multi_workspace_bytes(int64_t batch, int64_t n_rows, int64_t kv_len,
+                                            int32_t n_q_heads, int32_t head_dim);
+
+/*
  * Ragged (variable-length) batches of the three entry points: the same
  * contract, row by row, so a sequence's outputs are bit for bit those of the
  * dense call on that sequence alone.  (Rollout batches mix prompt and answer

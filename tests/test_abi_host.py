@@ -239,3 +239,29 @@ def test_prefill_varlen_lse_rejected_before_launch():
     assert f(Q, K, V, O, None, cu, 2, 32, 8, 128, SCALE, None) == INVALID
     assert f(Q, K, V, O, ctypes.c_void_p(L.value + 2), cu, 2, 32, 8, 128, SCALE, None) == ALIGN
     assert f(Q, K, V, O, ctypes.c_void_p(O.value + 64), cu, 2, 32, 8, 128, SCALE, None) == ALIAS
+
+
+def decode_multi(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, batch=1, rows=4, kv_len=2048, cap=4096, hq=32, hkv=8, d=128, scale=SCALE, ws=W,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    return kb.lib().kb_attn_decode_multi(a["q"], a["k"], a["v"], a["o"], a["batch"], a["rows"], a["kv_len"], a["cap"],
+                                         a["hq"], a["hkv"], a["d"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_multi_workspace_bytes():
+    assert kb.decode_multi_workspace_bytes(2, 3, 2048) == 2 * 32 * 3 * 2 * 130 * 4
+    assert kb.decode_multi_workspace_bytes(2, 3, 1024) == 0
+    assert kb.decode_multi_workspace_bytes(1, 1, 5000) == kb.decode_workspace_bytes(1, 5000)
+    assert kb.decode_multi_workspace_bytes(1, 9, 5000) == 0
+    assert kb.decode_multi_workspace_bytes(1, 4, 3) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(rows=0), UNSUPPORTED), (dict(rows=9), UNSUPPORTED), (dict(kv_len=3), LENGTH),
+    (dict(kv_len=4097), LENGTH), (dict(q=None), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=32 * 4 * 2 * 130 * 4 - 1), WORKSPACE),
+    (dict(o=Q), ALIAS), (dict(o=ctypes.c_void_p(O.value + 8)), ALIGN),
+])
+def test_decode_multi_rejected_before_launch(kw, expect):
+    assert decode_multi(**kw) == expect
