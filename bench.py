@@ -8,8 +8,9 @@ channels x8, V ~ N(0,1), scale 1/sqrt(128)):
      cached K/V                                           (prefill_kernel<true>)
   3. one-token decode at context 8192 (split-KV chunks + in-order combine)
 Inputs are resident in HBM before the timed region.  Outside the step the
-line also reports a decode sweep, a ragged batch, a paged-cache decode and the
-backward of the prefill (each with its own bitwise checks).  After timing, the
+line also reports a decode sweep, a ragged batch, a paged-cache decode, a
+multi-row decode and the backward of the prefill (each with its own bitwise
+checks).  After timing, the
 partitioned output and the decode output are compared bit for bit with the
 prefill output.
 
@@ -275,7 +276,7 @@ def main() -> int:
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
 
-    sweep, varlen, paged = None, None, None
+    sweep, varlen, paged, decode_multi = None, None, None, None
     if not args.no_extras:
         # decode sweep: batch 1/4/8/16 x context 128/1K/4K/8K over the resident
         # cache (capacity 16384, first kv_len keys), cold, one query token per head
@@ -377,6 +378,30 @@ def main() -> int:
                  "bitwise_mismatch_vs_dense_decode": int((opg.view(torch.int16)
                                                           != out_dec.view(B, HQ, D).view(torch.int16)).sum())}
         del kpool, vpool
+
+        # multi-row decode: the last 4 tokens of every sequence at context 8192
+        # (B=16) in one call, against the same rows of the prefill output
+        nr = 4
+        qm = qd[:, :, DEC_LEN - nr:DEC_LEN].contiguous()
+        om = torch.empty_like(qm)
+        wsm = torch.empty(max(1, kb.decode_multi_workspace_bytes(B, nr, DEC_LEN, HQ, D)), dtype=torch.uint8,
+                          device=dev)
+        mt = []
+        for _ in range(11):
+            flush.sum()
+            e0.record(stream)
+            kb.decode_multi(qm, kd, vd, kv_len=DEC_LEN, out=om, workspace=wsm)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mt.append(e0.elapsed_time(e1))
+        m_us = float(np.median(mt[1:])) * 1e3
+        m_bytes = 4096 * B * DEC_LEN + 16384 * B * nr
+        decode_multi = {"batch": B, "kv_len": DEC_LEN, "rows": nr, "us_cold": round(m_us, 2),
+                        "gbs": round(m_bytes / m_us / 1e3, 1),
+                        "frac_of_hbm_peak": round(m_bytes / (m_us * 1e-6) / PEAK_HBM, 4),
+                        "bitwise_mismatch_vs_prefill": int((om.view(torch.int16)
+                                                            != pre_bits[:, :, DEC_LEN - nr:DEC_LEN]).sum())}
+        del qm, om, wsm
     del flush
     backward = None if args.no_extras else backward_section(kb, torch, dev, qd, kd, vd, out_pre, reps=3, check=True)
 
@@ -418,6 +443,7 @@ def main() -> int:
         "decode_sweep": sweep,
         "varlen": varlen,
         "paged_decode": paged,
+        "decode_multi": decode_multi,
         "backward": backward,
         "bitwise_mismatch": {"partitioned_vs_prefill": mism, "decode_vs_prefill": mism_dec},
         "contract": kb.contract(),
