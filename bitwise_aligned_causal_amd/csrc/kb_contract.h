@@ -240,6 +240,30 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
     return r;
 }
 
+// max3 that is also ordered after `after` (an operand the instruction does not
+// read): used to start a chain of max3 reads of an MFMA result only once an
+// ordinary read of the same result has waited for it.
+__device__ __forceinline__ float max3_after(float a, float b, float c, float after) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c), "v"(after));
+    return r;
+}
+
+// Max of the 16 scores of one key block held by a lane, in four short
+// chains (the max is exact in any order).  The first read is ordinary code,
+// so the compiler waits for the block's products before it; every max3 is
+// ordered after it.
+__device__ __forceinline__ float block_max(const f32x16& s) {
+    float c0 = fmaxf(s[0], s[1]);
+    float c1 = max3_after(s[2], s[3], s[4], c0);
+    float c2 = max3_after(s[5], s[6], s[7], c0);
+    const float c3 = max3_after(s[8], s[9], s[10], c0);
+    c0 = max3(c0, s[11], s[12]);
+    c1 = max3(c1, s[13], s[14]);
+    c2 = max3(c2, s[15], c3);
+    return max3(c0, c1, c2);
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -274,25 +298,60 @@ constexpr float kLazyTau = 32.0f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Scores of one tile: S^T for key blocks 0 (s0) and 1 (s1).
-__device__ __forceinline__ void qk_tile(const bf16x8 (&qf)[8], const char* sK, int lane, f32x16& s0, f32x16& s1) {
+// Scores of one tile and the tile's max over both key blocks (masked where
+// kMask: key j > pos gives -inf).  Block 0's chain is issued first and block
+// 1's after it, each fragment read four products ahead; block 0's mask and
+// max run between block 1's products.  The order is fixed with scheduling
+// fences.
+template <bool kMask>
+__device__ __forceinline__ float qk_tile_max(const bf16x8 (&qf)[8], const char* sK, int lane, int64_t key0,
+                                             int64_t pos, f32x16& s0, f32x16& s1) {
+    const int h = lane >> 5;
+    const float ninf = -__builtin_inff();
     s0 = zero16();
     s1 = zero16();
+    bf16x8 kf[4];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-        const bf16x8 k0 = k_frag(sK, 0, st, lane);
-        const bf16x8 k1 = k_frag(sK, 1, st, lane);
-        s0 = mfma(k0, qf[st], s0);
-        s1 = mfma(k1, qf[st], s1);
-    }
-    // schedule: 8 fragment reads ahead, then 2 MFMAs per 2 reads
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    for (int i = 0; i < 4; ++i) kf[i] = k_frag(sK, 0, i, lane);
+    float c0 = 0.0f, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int i = 0; i < 16; ++i) {
+        if (i < 8)
+            s0 = mfma(kf[i & 3], qf[i & 7], s0);
+        else
+            s1 = mfma(kf[i & 3], qf[i & 7], s1);
+        if (i + 4 < 16) kf[i & 3] = k_frag(sK, (i + 4) >> 3, (i + 4) & 7, lane);
+        if (i == 9) {
+            if (kMask) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    s0[v] = kk > pos ? ninf : s0[v];
+                }
+            }
+            c0 = fmaxf(s0[0], s0[1]);
+            c1 = max3_after(s0[2], s0[3], s0[4], c0);
+        } else if (i == 10) {
+            c2 = max3_after(s0[5], s0[6], s0[7], c0);
+            c3 = max3_after(s0[8], s0[9], s0[10], c0);
+        } else if (i == 11) {
+            c0 = max3(c0, s0[11], s0[12]);
+            c1 = max3(c1, s0[13], s0[14]);
+        } else if (i == 12) {
+            c2 = max3(c2, s0[15], c3);
+            c0 = max3(c0, c1, c2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if (kMask) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t kk = key0 + 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            s1[v] = kk > pos ? ninf : s1[v];
+        }
+    }
+    const float m1 = block_max(s1);
+    return max3(c0, m1, m1);
 }
 
 // o *= a.  o * 1 == o exactly, so skipping the multiply when no column of
@@ -349,21 +408,8 @@ template <int NDB, bool kMask, bool kFirst = false>
 __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
                                           int64_t key0, int64_t pos, float c, float& mc, float& l,
                                           f32x16 (&o)[NDB], int dblk0) {
-    const int h = lane >> 5;
     f32x16 s0, s1;
-    qk_tile(qf, sK, lane, s0, s1);
-    if (kMask) {
-        const float ninf = -__builtin_inff();
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
-            s0[v] = kk > pos ? ninf : s0[v];
-            s1[v] = kk + 32 > pos ? ninf : s1[v];
-        }
-    }
-    float mt = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mt = max3(mt, s0[v], s1[v]);
+    float mt = qk_tile_max<kMask>(qf, sK, lane, key0, pos, s0, s1);
     {
         float lo, hi;
         halves(mt, lo, hi);
