@@ -228,40 +228,21 @@ __device__ __forceinline__ void halves(float x, float& lo, float& hi) {
     hi = __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// max of three floats (exact; written as one instruction so that no
-// canonicalising moves are inserted for MFMA results).  The compiler does not
-// see inside the asm, so it would not wait for an MFMA result read here: the
-// first read of every score block is ordinary code (the fmaxf that starts the
-// max tree), which makes the compiler wait for the products; max3 then reads
-// registers that are already complete.
-__device__ __forceinline__ float max3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
+// IEEE maximum (v_maximum_f32 / v_maximum3_f32): exact, and unlike fmaxf it
+// needs no canonicalising moves in front of MFMA results.  The scores are
+// finite or -inf, so it agrees with any other max.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-// max3 that is also ordered after `after` (an operand the instruction does not
-// read): used to start a chain of max3 reads of an MFMA result only once an
-// ordinary read of the same result has waited for it.
-__device__ __forceinline__ float max3_after(float a, float b, float c, float after) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c), "v"(after));
-    return r;
-}
-
-// Max of the 16 scores of one key block held by a lane, in four short
-// chains (the max is exact in any order).  The first read is ordinary code,
-// so the compiler waits for the block's products before it; every max3 is
-// ordered after it.
+// Max of the 16 scores of one key block held by a lane, in four short chains
+// of three-input maxima (the max is exact in any order).
 __device__ __forceinline__ float block_max(const f32x16& s) {
-    float c0 = fmaxf(s[0], s[1]);
-    float c1 = max3_after(s[2], s[3], s[4], c0);
-    float c2 = max3_after(s[5], s[6], s[7], c0);
-    const float c3 = max3_after(s[8], s[9], s[10], c0);
-    c0 = max3(c0, s[11], s[12]);
-    c1 = max3(c1, s[13], s[14]);
-    c2 = max3(c2, s[15], c3);
-    return max3(c0, c1, c2);
+    float c0 = vmax(vmax(s[0], s[1]), s[2]);
+    float c1 = vmax(vmax(s[3], s[4]), s[5]);
+    float c2 = vmax(vmax(s[6], s[7]), s[8]);
+    float c3 = vmax(vmax(s[9], s[10]), s[11]);
+    c0 = vmax(vmax(c0, s[12]), s[13]);
+    c1 = vmax(vmax(c1, s[14]), s[15]);
+    return vmax(vmax(c0, c1), vmax(c2, c3));
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -329,17 +310,16 @@ __device__ __forceinline__ float qk_tile_max(const bf16x8 (&qf)[8], const char* 
                     s0[v] = kk > pos ? ninf : s0[v];
                 }
             }
-            c0 = fmaxf(s0[0], s0[1]);
-            c1 = max3_after(s0[2], s0[3], s0[4], c0);
+            c0 = vmax(vmax(s0[0], s0[1]), s0[2]);
+            c1 = vmax(vmax(s0[3], s0[4]), s0[5]);
         } else if (i == 10) {
-            c2 = max3_after(s0[5], s0[6], s0[7], c0);
-            c3 = max3_after(s0[8], s0[9], s0[10], c0);
+            c2 = vmax(vmax(s0[6], s0[7]), s0[8]);
+            c3 = vmax(vmax(s0[9], s0[10]), s0[11]);
         } else if (i == 11) {
-            c0 = max3(c0, s0[11], s0[12]);
-            c1 = max3(c1, s0[13], s0[14]);
+            c0 = vmax(vmax(c0, s0[12]), s0[13]);
+            c1 = vmax(vmax(c1, s0[14]), s0[15]);
         } else if (i == 12) {
-            c2 = max3(c2, s0[15], c3);
-            c0 = max3(c0, c1, c2);
+            c0 = vmax(vmax(c0, c1), vmax(c2, c3));
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -351,7 +331,7 @@ __device__ __forceinline__ float qk_tile_max(const bf16x8 (&qf)[8], const char* 
         }
     }
     const float m1 = block_max(s1);
-    return max3(c0, m1, m1);
+    return vmax(c0, m1);
 }
 
 // o *= a.  o * 1 == o exactly, so skipping the multiply when no column of
@@ -413,7 +393,7 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
     {
         float lo, hi;
         halves(mt, lo, hi);
-        mt = fmaxf(lo, hi);
+        mt = vmax(lo, hi);
     }
     const float mtc = mt * c;
     const bool grow = (mtc - mc) > kLazyTau;
