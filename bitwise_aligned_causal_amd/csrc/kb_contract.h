@@ -20,9 +20,9 @@
 //     mtc   = (max_j s_j) * c                         with c = fp32(scale * log2 e)
 //     grow  = mtc - mc > 32;  mc' = grow ? mtc : mc;  a = grow ? exp2(mc - mc') : 1
 //     p_j   = exp2(fma(s_j, c, -mc'));  P_j = bf16_rne(p_j)   (P_j <= 2^32)
-//     l     = fma(l, a, sum(P))   sum: per 16-key step, a chain of 4 bf16 dot2
-//             with (1, 1); then ((k0u0 + k0u1) + (k1u0 + k1u1)) per lane half,
-//             then (low half + high half)
+//     l     = fma(l, a, sum(P))   sum: per lane half, one chain of 16 bf16
+//             dot2 with (1, 1) over the key steps (0,0), (0,1), (1,0), (1,1)
+//             in order, 4 per step; then (low half + high half)
 //     o     = o * a;  o = MFMA chain over the tile's 4 key steps in order
 //     mc    = mc'
 //   per chunk, in chunk order (first chunk is copied, the rest folded):
@@ -347,10 +347,9 @@ __device__ __forceinline__ void rescale_o(f32x16 (&o)[NDB], float a, bool any_gr
     }
 }
 
-// P of one 16-key step (kb, u): 8 exps, 4 paired converts, and the step's
-// chain of 4 dot2 row-sum partials.
-__device__ __forceinline__ void p_step(const f32x16& s, int u, float c, float nmc, bf16x8& pf, float& part) {
-    float acc = 0.0f;
+// P of one 16-key step (kb, u): 8 exps and 4 paired converts; the step's 4
+// dot2 row-sum terms continue the lane's chain `acc`.
+__device__ __forceinline__ void p_step(const f32x16& s, int u, float c, float nmc, bf16x8& pf, float& acc) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         f32x2 pp;
@@ -362,7 +361,6 @@ __device__ __forceinline__ void p_step(const f32x16& s, int u, float c, float nm
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         acc = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, acc, false);
     }
-    part = acc;
 }
 
 // o += P V for one 16-key step (kb, u) over the wave's NDB d blocks.
@@ -403,8 +401,8 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
     const float nmc = -mcn;
 
     bf16x8 pf[2][2];
-    float part[2][2];
-    p_step(s0, 0, c, nmc, pf[0][0], part[0][0]);
+    float acc = 0.0f;  // this lane's row-sum chain over the tile's 16 dot2 terms
+    p_step(s0, 0, c, nmc, pf[0][0], acc);
     if (kFirst) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] = zero16();
@@ -412,17 +410,16 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
         rescale_o<NDB>(o, a, any_grow);
     }
     pv_step<NDB>(pf[0][0], sV, 0, 0, lane, o, dblk0);
-    p_step(s0, 1, c, nmc, pf[0][1], part[0][1]);
+    p_step(s0, 1, c, nmc, pf[0][1], acc);
     pv_step<NDB>(pf[0][1], sV, 0, 1, lane, o, dblk0);
-    p_step(s1, 0, c, nmc, pf[1][0], part[1][0]);
+    p_step(s1, 0, c, nmc, pf[1][0], acc);
     pv_step<NDB>(pf[1][0], sV, 1, 0, lane, o, dblk0);
-    p_step(s1, 1, c, nmc, pf[1][1], part[1][1]);
+    p_step(s1, 1, c, nmc, pf[1][1], acc);
     pv_step<NDB>(pf[1][1], sV, 1, 1, lane, o, dblk0);
 
-    // fixed tree: ((00 + 01) + (10 + 11)) per lane half, then (low + high)
-    const float ls_half = (part[0][0] + part[0][1]) + (part[1][0] + part[1][1]);
+    // the two lane halves of the column: (low + high)
     float ls_lo, ls_hi;
-    halves(ls_half, ls_lo, ls_hi);
+    halves(acc, ls_lo, ls_hi);
     const float ls = ls_lo + ls_hi;
     l = __builtin_fmaf(l, a, ls);
     mc = mcn;
