@@ -61,7 +61,8 @@ struct PrefillWork {
 // absolute positions [64 pb, 64 pb + 64).  Every row of the block has its last
 // visible key in tile pb, so all rows visit exactly the tiles 0..pb and never
 // a tile that is fully masked for them.  K/V tiles are shared by the 8 waves
-// through a 3-stage LDS ring filled by direct loads two tiles ahead.
+// through a 3-stage LDS ring (padded rows, PaddedTile) filled by direct loads two
+// tiles ahead.
 // kPartitioned = false is the full-sequence case (q_len == kv_len, row r at
 // position r); both instantiations run the same per-row arithmetic.
 template <bool kPartitioned>
@@ -81,11 +82,11 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
     const int64_t kv_len = wk.kv_len;
     const int t_last = pb;
 
-    StagePlan<kPrefillWaves> plan;
+    StagePlan<PaddedTile, kPrefillWaves> plan;
     stage_plan(plan, lane, w);
-    stage_tile(plan, kbase, vbase, 0, kv_len, smem, smem + kKBytes, lane, w);
+    stage_tile(plan, kbase, vbase, 0, kv_len, smem, lane, w);
     if (t_last >= 1)
-        stage_tile(plan, kbase, vbase, kTile, kv_len, smem + kTileBytes, smem + kTileBytes + kKBytes, lane, w);
+        stage_tile(plan, kbase, vbase, kTile, kv_len, smem + PaddedTile::kBytes, lane, w);
 
     const int64_t qrow0 = (int64_t)(w & 3) * wk.q_hstride;  // this wave's query head
     bf16x8 qf[8];
@@ -115,13 +116,13 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
     // start the loads of tile t + 2 into the stage nobody reads any more.
     auto publish = [&](int t) {
         if (t + 1 <= t_last)
-            wait_vm<kTileLoads / kPrefillWaves>();
+            wait_stage_loads<PaddedTile, kPrefillWaves>(w);
         else
             wait_vm<0>();
         __syncthreads();
         if (t + 2 <= t_last) {
-            char* nb = smem + ((t + 2) % kStages) * kTileBytes;
-            stage_tile(plan, kbase, vbase, (int64_t)(t + 2) * kTile, kv_len, nb, nb + kKBytes, lane, w);
+            char* nb = smem + ((t + 2) % kStages) * PaddedTile::kBytes;
+            stage_tile(plan, kbase, vbase, (int64_t)(t + 2) * kTile, kv_len, nb, lane, w);
         }
     };
     auto close_chunk = [&]() {
@@ -153,22 +154,25 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
     for (int t0 = 0; t0 < t_last; t0 += kTilesPerChunk) {
         {
             publish(t0);
-            const char* buf = smem + (t0 % kStages) * kTileBytes;
-            tile_step<4, false, true>(qf, buf, buf + kKBytes, lane, (int64_t)t0 * kTile, pos, c, mc, l, acc, 0);
+            const char* buf = smem + (t0 % kStages) * PaddedTile::kBytes;
+            tile_step<PaddedTile, 4, false, true>(qf, buf, buf + PaddedTile::kKStage, lane, (int64_t)t0 * kTile, pos, c,
+                                                  mc, l, acc, 0);
         }
         const int t_end = min(t0 + kTilesPerChunk, t_last);
         for (int t = t0 + 1; t < t_end; ++t) {
             publish(t);
-            const char* buf = smem + (t % kStages) * kTileBytes;
-            tile_step<4, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, 0);
+            const char* buf = smem + (t % kStages) * PaddedTile::kBytes;
+            tile_step<PaddedTile, 4, false>(qf, buf, buf + PaddedTile::kKStage, lane, (int64_t)t * kTile, pos, c, mc, l,
+                                            acc, 0);
         }
         if (t_end == t0 + kTilesPerChunk) close_chunk();
     }
     // the diagonal tile t_last holds keys beyond some rows' positions
     {
         publish(t_last);
-        const char* buf = smem + (t_last % kStages) * kTileBytes;
-        tile_step<4, true>(qf, buf, buf + kKBytes, lane, (int64_t)t_last * kTile, pos, c, mc, l, acc, 0);
+        const char* buf = smem + (t_last % kStages) * PaddedTile::kBytes;
+        tile_step<PaddedTile, 4, true>(qf, buf, buf + PaddedTile::kKStage, lane, (int64_t)t_last * kTile, pos, c, mc, l,
+                                       acc, 0);
         close_chunk();
     }
 
@@ -193,7 +197,7 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
 // Dense batch: q, o [batch, Hq, q_len, 128]; k, v [batch, Hkv, cap, 128].
 template <bool kPartitioned>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * PaddedTile::kBytes];
     const int nbg = a.batch * a.n_kv_heads;
     const int x = blockIdx.x;
     int bg, pbr;
@@ -253,7 +257,7 @@ struct VarlenArgs {
 // Work units of a sequence: (64-position block, KV head), longest blocks
 // first.  All rows use the partitioned form (q_len == kv_len gives position r).
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_varlen_kernel(VarlenArgs a, VarlenTable t) {
-    __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * PaddedTile::kBytes];
     const int x = blockIdx.x;
     int s = 0;
     while (s + 1 < t.n_seqs && t.unit0[s + 1] <= x) ++s;
@@ -297,7 +301,8 @@ constexpr int kDecodeStages = 2;
 
 // Wait until at most `ahead` tiles of this wave's decode loads are pending.
 __device__ __forceinline__ void wait_tiles_decode(int ahead) {
-    constexpr int per = kTileLoads / kDecodeWaves;
+    constexpr int per = SwizzledTile::kLoads / kDecodeWaves;
+    static_assert(SwizzledTile::kLoads % kDecodeWaves == 0, "every wave issues the same loads");
     switch (ahead) {
         case 0: wait_vm<0>(); break;
         case 1: wait_vm<per>(); break;
@@ -358,7 +363,7 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
     // later chunk every key is masked for it and its column is not stored
     const bool active = col && pos >= (int64_t)t0 * kTile;
 
-    StagePlan<kDecodeWaves> plan;
+    StagePlan<SwizzledTile, kDecodeWaves> plan;
     stage_plan(plan, lane, w);
 
     // paged: lane i holds the pool index of the chunk's i-th page (at most 16)
@@ -374,17 +379,17 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
             const int64_t key0 = (int64_t)t * kTile;
             const int page = __builtin_amdgcn_readlane(pg, (int)(key0 / wk.page_size) - p0);
             const int64_t off = (int64_t)page * wk.page_elems + wk.head_elems + (key0 % wk.page_size) * kHeadDim;
-            stage_tile(plan, wk.kpool + off, wk.vpool + off, 0, min((int64_t)kTile, kv_len - key0), nb, nb + kKBytes,
+            stage_tile(plan, wk.kpool + off, wk.vpool + off, 0, min((int64_t)kTile, kv_len - key0), nb,
                        lane, w);
         } else {
-            stage_tile(plan, kbase, vbase, (int64_t)t * kTile, kv_len, nb, nb + kKBytes, lane, w);
+            stage_tile(plan, kbase, vbase, (int64_t)t * kTile, kv_len, nb, lane, w);
         }
     };
 
     // ring of kDecodeStages tiles, loads kDecodeStages - 1 tiles ahead
 #pragma unroll
     for (int i = 0; i < kDecodeStages - 1; ++i) {
-        if (t0 + i < t1) stage(t0 + i, smem + i * kTileBytes);
+        if (t0 + i < t1) stage(t0 + i, smem + i * SwizzledTile::kBytes);
     }
 
     const int64_t qrow_idx = wk.q_row0 + (int64_t)hi * wk.q_hstride + ri;
@@ -408,14 +413,17 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
         wait_tiles_decode(ahead);
         __syncthreads();
         if (t + kDecodeStages - 1 < t1)
-            stage(t + kDecodeStages - 1, smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * kTileBytes);
-        const char* buf = smem + ((t - t0) % kDecodeStages) * kTileBytes;
+            stage(t + kDecodeStages - 1,
+                  smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * SwizzledTile::kBytes);
+        const char* buf = smem + ((t - t0) % kDecodeStages) * SwizzledTile::kBytes;
         // a tile needs the mask when it holds keys beyond the first row's
         // position (only the context's last tile when n_rows = 1)
         if (t < n_tiles - 1 && (int64_t)t * kTile + kTile - 1 <= kv_len - n_rows)
-            tile_step<1, false>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, w);
+            tile_step<SwizzledTile, 1, false>(qf, buf, buf + SwizzledTile::kKStage, lane, (int64_t)t * kTile, pos, c, mc,
+                                              l, acc, w);
         else
-            tile_step<1, true>(qf, buf, buf + kKBytes, lane, (int64_t)t * kTile, pos, c, mc, l, acc, w);
+            tile_step<SwizzledTile, 1, true>(qf, buf, buf + SwizzledTile::kKStage, lane, (int64_t)t * kTile, pos, c, mc,
+                                             l, acc, w);
     }
 
     if (!active) return;
@@ -453,7 +461,7 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
 
 // Dense batch: q, o [batch, Hq, 1, 128]; caches [batch, Hkv, cap, 128].
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * SwizzledTile::kBytes];
     const int x = blockIdx.x;
     const int chunk = x % a.n_chunks;
     const int bg = x / a.n_chunks;
@@ -550,7 +558,7 @@ struct DecodeVarlenArgs {
 
 template <bool kPaged>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_varlen_kernel(DecodeVarlenArgs a, DecodeVarlenTable t) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * SwizzledTile::kBytes];
     const int x = blockIdx.x;
     int s = 0;
     while (s + 1 < t.n_seqs && t.unit0[s + 1] <= x) ++s;

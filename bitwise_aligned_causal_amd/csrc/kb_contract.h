@@ -51,89 +51,146 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// ---------------------------------------------------------------------------
-// LDS tile layout (one K/V tile of 64 keys), both row-major, 256 B per key:
-//   K  16-byte chunk c of key row r at chunk position c ^ (r & 15)
-//      (the A-operand reads, 16 rows x one chunk per 16 lanes, hit 16
-//      distinct bank groups)
-//   V  16-byte chunk c of key row r at chunk position c ^ ((r & 3) << 2)
-//      (the transposing reads touch 4 rows x 4 chunks per 32 lanes)
-// Tiles are filled by global_load_lds_dwordx4: lane L of an instruction
-// lands at the instruction's LDS base + 16 L, so each lane fetches the global
-// chunk that belongs at its LDS position.  Keys at or beyond kv_len read the
-// (valid) row kv_len - 1 instead: those keys are masked (K) or weighted by
-// P = 0 (V), so only finite values ever enter the products.
-// ---------------------------------------------------------------------------
+// Unpadded K/V tile sizes (64 keys x 256 B rows each); the backward kernels
+// stage their tiles in this size with layouts of their own.
 constexpr int kKBytes = kTile * kHeadDim * 2;
 constexpr int kVBytes = kTile * kHeadDim * 2;
 constexpr int kTileBytes = kKBytes + kVBytes;
 constexpr int kTileLoads = kTileBytes / 1024;  // 32 one-KiB direct loads
 
-__device__ __forceinline__ int k_swz(int row) { return row & 15; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
-
-// Issue this wave's share of the 32 one-KiB direct loads of a tile:
-// instructions i = wave, wave + n_waves, ... (0..15 fill K rows 4i..4i+3,
-// 16..31 fill V rows 4(i-16)..+3).  The loads are issued as inline assembly
-// so that the compiler does not serialise every later LDS read behind them;
-// completion is tracked explicitly with wait_vm() before the workgroup
-// barrier that publishes the tile.
-__device__ __forceinline__ void stage_issue(const uint16_t* kbase, const uint16_t* vbase, int64_t key0,
-                                            int64_t kv_len, char* sK, char* sV, int lane, int wave,
-                                            int n_waves) {
-    for (int i = wave; i < kTileLoads; i += n_waves) {
-        const bool is_v = i >= 16;
-        const int row = 4 * (i & 15) + (lane >> 4);
-        const int pc = lane & 15;
-        const int c = pc ^ (is_v ? v_swz(row) : k_swz(row));
-        int64_t key = key0 + row;
-        key = key < kv_len ? key : kv_len - 1;
-        const uint16_t* src = (is_v ? vbase : kbase) + key * kHeadDim + c * 8;
-        const char* dst = (is_v ? sV : sK) + 1024 * (i & 15);
-        const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-        uint32_t saved_m0;
-        // M0 is saved and restored around the load; s_nop covers the one
-        // wait state required between an M0 write and an LDS-DMA load
-        asm volatile(
-            "s_mov_b32 %0, m0\n\t"
-            "s_mov_b32 m0, %2\n\t"
-            "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %1, off\n\t"
-            "s_nop 0\n\t"
-            "s_mov_b32 m0, %0"
-            : "=&s"(saved_m0)
-            : "v"(src), "s"(lds_base)
-            : "memory");
-    }
+__device__ __forceinline__ bf16x8 lds_read16(const char* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-// Per-wave plan of the direct loads of a tile for a workgroup of NW waves:
-// wave w issues instructions i = w, w + NW, ...; the first half of them fill
-// K, the second half V.  off[k] is the byte offset, from the tile's first key
-// row, of the 16-byte chunk lane L fetches in its k-th instruction; it does
-// not depend on the tile, so it is computed once.
-template <int NW>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x8 tr_pair(const char* p0, const char* p1) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 all = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, all);
+}
+
+// ---------------------------------------------------------------------------
+// LDS layouts of one K/V tile (one stage of a ring): K, then V.  Which one a
+// kernel uses changes no value it reads, so no bit of any output.  Both are
+// filled by one-KiB direct loads (global_load_lds_dwordx4): lane L of load i
+// lands at byte 1024 i + 16 L of the stage and fetches the 16-byte chunk of K
+// or V that belongs there.  The fragment readers, for every layout:
+//   k_frag   A operand of S^T = K Q^T for key block kb, k-step st:
+//            lane (key j, half h) holds K[32kb + j][16st + 8h .. +7]
+//   vt_frag  A operand of O^T += V^T P^T for key step (kb, u), d block dblk:
+//            lane (d = 32 dblk + j, half h) holds, in slot order,
+//            V[K0 + 4h + {0..3}][d], V[K0 + 8 + 4h + {0..3}][d], K0 = 32kb + 16u,
+//            read with two ds_read_b64_tr_b16.  Within each 16-lane group,
+//            lane i of the result takes element (i & 3) of the 8-byte blocks
+//            read by lanes 4n + (i >> 2) (n = 0..3), so lane L = 16 g + 4 n + jj
+//            reads V[K0 + 4 (g >> 1) + n][32 dblk + 16 (g & 1) + 4 jj .. +3].
+// ---------------------------------------------------------------------------
+
+// Padded rows (the prefill): every fragment read is a per-lane base plus a
+// constant, so no address arithmetic runs per tile.
+//   K  key row r at r * 272 bytes (16 B of padding): the 16 rows read by 16
+//      lanes of one A-operand read start 68 words apart, i.e. in 16 distinct
+//      groups of 4 banks
+//   V  key row r at r * 320 bytes (64 B of padding): a transposing read
+//      touches 4 rows x 32 B per 32 lanes, rows 80 words apart, i.e. all 64
+//      banks once
+// 37 loads per stage (17 for K, 20 for V); padding slots fetch chunk 15 of
+// their row, which nothing reads.
+struct PaddedTile {
+    static constexpr int kKRow = 272;
+    static constexpr int kVRow = 320;
+    static constexpr int kKStage = kTile * kKRow;  // 17408
+    static constexpr int kBytes = kKStage + kTile * kVRow;  // 37888
+    static constexpr int kLoads = kBytes / 1024;  // 37
+    static constexpr int kKLoads = kKStage / 1024;  // 17
+
+    // source offset, from the tile's first key row, of load i, lane `lane`
+    __device__ static __forceinline__ uint32_t src(int i, int lane, int& row, bool& v) {
+        v = i >= kKLoads;
+        const int p = (v ? i - kKLoads : i) * 64 + lane;  // 16-byte slot in the operand
+        const int per = v ? kVRow / 16 : kKRow / 16;       // slots per row (20 or 17)
+        row = p / per;
+        const int c = min(p - row * per, 15);
+        return (uint32_t)(row * 256 + c * 16);
+    }
+    __device__ static __forceinline__ bf16x8 k_frag(const char* sK, int kb, int st, int lane) {
+        const char* base = sK + (lane & 31) * kKRow + (lane >> 5) * 16;
+        return lds_read16(base + kb * 32 * kKRow + st * 32);
+    }
+    __device__ static __forceinline__ bf16x8 vt_frag(const char* sV, int kb, int u, int dblk, int lane) {
+        const int g = lane >> 4, n = (lane >> 2) & 3, jj = lane & 3;
+        const char* base = sV + (4 * (g >> 1) + n) * kVRow + (16 * (g & 1) + 4 * jj) * 2;
+        const char* p0 = base + (32 * kb + 16 * u) * kVRow + 64 * dblk;
+        return tr_pair(p0, p0 + 8 * kVRow);
+    }
+};
+
+// Swizzled 256-byte rows (the decode, which streams HBM and wants the fewest
+// loads per tile): 32 loads per stage.
+//   K  16-byte chunk c of key row r at chunk position c ^ (r & 15) (the
+//      A-operand reads, 16 rows x one chunk per 16 lanes, hit 16 distinct
+//      bank groups)
+//   V  16-byte chunk c of key row r at chunk position c ^ ((r & 3) << 2)
+//      (the transposing reads touch 4 rows x 4 chunks per 32 lanes)
+struct SwizzledTile {
+    static constexpr int kKStage = kTile * 256;
+    static constexpr int kBytes = 2 * kKStage;  // 32768
+    static constexpr int kLoads = kBytes / 1024;  // 32
+    static constexpr int kKLoads = kKStage / 1024;  // 16
+
+    __device__ static __forceinline__ int k_swz(int row) { return row & 15; }
+    __device__ static __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+    __device__ static __forceinline__ uint32_t src(int i, int lane, int& row, bool& v) {
+        v = i >= kKLoads;
+        row = 4 * (i & 15) + (lane >> 4);
+        const int c = (lane & 15) ^ (v ? v_swz(row) : k_swz(row));
+        return (uint32_t)(row * 256 + c * 16);
+    }
+    __device__ static __forceinline__ bf16x8 k_frag(const char* sK, int kb, int st, int lane) {
+        const int row = 32 * kb + (lane & 31);
+        const int c = 2 * st + (lane >> 5);
+        return lds_read16(sK + row * 256 + ((c ^ k_swz(row)) << 4));
+    }
+    __device__ static __forceinline__ bf16x8 vt_frag(const char* sV, int kb, int u, int dblk, int lane) {
+        const int g = lane >> 4, n = (lane >> 2) & 3, jj = lane & 3;
+        const int row0 = 32 * kb + 16 * u + 4 * (g >> 1) + n;
+        const int d = 32 * dblk + 16 * (g & 1) + 4 * jj;
+        const int c = d >> 3, half = (d & 4) << 1;  // byte offset 0 or 8 inside the chunk
+        const int row1 = row0 + 8;
+        return tr_pair(sV + row0 * 256 + ((c ^ v_swz(row0)) << 4) + half,
+                       sV + row1 * 256 + ((c ^ v_swz(row1)) << 4) + half);
+    }
+};
+
+// Per-wave plan of the direct loads of a stage for a workgroup of NW waves:
+// wave w issues loads i = w, w + NW, ... < L::kLoads.  off[k] is lane L's
+// source offset for its k-th load; it does not depend on the tile.
+template <class L, int NW>
 struct StagePlan {
-    static constexpr int kN = kTileLoads / NW;
-    static_assert(kTileLoads % NW == 0 && NW <= 16, "each wave issues whole K and V halves");
+    static constexpr int kN = (L::kLoads + NW - 1) / NW;
     uint32_t off[kN];
 };
 
-template <int NW>
-__device__ __forceinline__ void stage_plan(StagePlan<NW>& p, int lane, int wave) {
+template <class L, int NW>
+__device__ __forceinline__ void stage_plan(StagePlan<L, NW>& p, int lane, int wave) {
 #pragma unroll
-    for (int k = 0; k < StagePlan<NW>::kN; ++k) {
+    for (int k = 0; k < StagePlan<L, NW>::kN; ++k) {
         const int i = wave + k * NW;
-        const bool is_v = k >= StagePlan<NW>::kN / 2;
-        const int row = 4 * (i & 15) + (lane >> 4);
-        const int c = (lane & 15) ^ (is_v ? v_swz(row) : k_swz(row));
-        p.off[k] = (uint32_t)(row * 256 + c * 16);
+        int row;
+        bool v;
+        p.off[k] = i < L::kLoads ? L::src(i, lane, row, v) : 0u;
     }
 }
 
 __device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, const char* dst) {
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
     uint32_t saved_m0;
+    // M0 is saved and restored around the load; s_nop covers the one wait
+    // state required between an M0 write and an LDS-DMA load
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %3\n\t"
@@ -146,31 +203,51 @@ __device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, cons
         : "memory");
 }
 
-// Issue this wave's loads of the tile starting at key0, which must lie wholly
-// below kv_len: a scalar tile base plus the planned per-lane offsets.
-template <int NW>
-__device__ __forceinline__ void stage_issue_full(const StagePlan<NW>& p, const uint16_t* kbase,
-                                                 const uint16_t* vbase, int64_t key0, char* sK, char* sV,
-                                                 int wave) {
-    const char* kt = reinterpret_cast<const char*>(kbase + key0 * kHeadDim);
-    const char* vt = reinterpret_cast<const char*>(vbase + key0 * kHeadDim);
-#pragma unroll
-    for (int k = 0; k < StagePlan<NW>::kN; ++k) {
-        const int i = wave + k * NW;
-        const bool is_v = k >= StagePlan<NW>::kN / 2;
-        lds_dma16(is_v ? vt : kt, p.off[k], (is_v ? sV : sK) + 1024 * (i & 15));
-    }
+__device__ __forceinline__ void lds_dma16_flat(const void* src, const char* dst) {
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(src), "s"(lds_base)
+        : "memory");
 }
 
-// Either form, chosen per tile (uniform branch).
-template <int NW>
-__device__ __forceinline__ void stage_tile(const StagePlan<NW>& p, const uint16_t* kbase, const uint16_t* vbase,
-                                           int64_t key0, int64_t kv_len, char* sK, char* sV, int lane,
-                                           int wave) {
-    if (key0 + kTile <= kv_len)
-        stage_issue_full<NW>(p, kbase, vbase, key0, sK, sV, wave);
-    else
-        stage_issue(kbase, vbase, key0, kv_len, sK, sV, lane, wave, NW);
+// Issue this wave's loads of the tile starting at key0 into the stage at
+// `stage` (K at stage, V at stage + L::kKStage).  A tile wholly below kv_len
+// takes the planned offsets from a scalar tile base; otherwise keys at or
+// beyond kv_len read the (valid) row kv_len - 1 instead: those keys are
+// masked (K) or weighted by P = 0 (V), so only finite values ever enter the
+// products.  The loads are inline assembly so that the compiler does not
+// serialise later LDS reads behind them; completion is tracked with wait_vm()
+// before the workgroup barrier that publishes the tile.
+template <class L, int NW>
+__device__ __forceinline__ void stage_tile(const StagePlan<L, NW>& p, const uint16_t* kbase, const uint16_t* vbase,
+                                           int64_t key0, int64_t kv_len, char* stage, int lane, int wave) {
+    const char* kt = reinterpret_cast<const char*>(kbase + key0 * kHeadDim);
+    const char* vt = reinterpret_cast<const char*>(vbase + key0 * kHeadDim);
+    if (key0 + kTile <= kv_len) {
+#pragma unroll
+        for (int k = 0; k < StagePlan<L, NW>::kN; ++k) {
+            const int i = wave + k * NW;
+            if (k == StagePlan<L, NW>::kN - 1 && i >= L::kLoads) break;
+            lds_dma16(i >= L::kKLoads ? vt : kt, p.off[k], stage + 1024 * i);
+        }
+    } else {
+        for (int i = wave; i < L::kLoads; i += NW) {
+            int row;
+            bool v;
+            const uint32_t off = L::src(i, lane, row, v);
+            const int64_t keep = key0 + row < kv_len ? 0 : (key0 + row - (kv_len - 1)) * 256;
+            const char* src = (v ? vt : kt) + (off - keep);
+            lds_dma16_flat(src, stage + 1024 * i);
+        }
+    }
 }
 
 // Wait until at most N of this wave's vector-memory operations are pending.
@@ -180,41 +257,14 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ bf16x8 lds_read16(const char* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-// A operand of S^T = K Q^T for key block kb, k-step st:
-// lane (key j, half h) holds K[32kb + j][16st + 8h .. +7]
-__device__ __forceinline__ bf16x8 k_frag(const char* sK, int kb, int st, int lane) {
-    const int row = 32 * kb + (lane & 31);
-    const int c = 2 * st + (lane >> 5);
-    return lds_read16(sK + row * 256 + ((c ^ k_swz(row)) << 4));
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// A operand of O^T += V^T P^T for key step (kb, u) and d block dblk:
-// lane (d = 32 dblk + j, half h) holds, in slot order,
-//   V[K0 + 4h + {0..3}][d], V[K0 + 8 + 4h + {0..3}][d]      with K0 = 32kb + 16u
-// read with two ds_read_b64_tr_b16.  Within each 16-lane group, lane i of the
-// result takes element (i & 3) of the 8-byte blocks read by lanes 4n + (i >> 2)
-// (n = 0..3), so lane L = 16 g + 4 n + jj reads V[K0 + 4 (g >> 1) + n][32 dblk +
-// 16 (g & 1) + 4 jj .. +3].
-__device__ __forceinline__ bf16x8 vt_frag(const char* sV, int kb, int u, int dblk, int lane) {
-    const int g = lane >> 4, n = (lane >> 2) & 3, jj = lane & 3;
-    const int row0 = 32 * kb + 16 * u + 4 * (g >> 1) + n;
-    const int d = 32 * dblk + 16 * (g & 1) + 4 * jj;
-    const int c = d >> 3, half = (d & 4) << 1;  // byte offset 0 or 8 inside the chunk
-    const int row1 = row0 + 8;
-    const char* p0 = sV + row0 * 256 + ((c ^ v_swz(row0)) << 4) + half;
-    const char* p1 = sV + row1 * 256 + ((c ^ v_swz(row1)) << 4) + half;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 all = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, all);
+// Wait until at most one stage of this wave's direct loads is pending: the
+// loads of the tile after the one being published may stay in flight.
+template <class L, int NW>
+__device__ __forceinline__ void wait_stage_loads(int wave) {
+    if (wave < L::kLoads % NW)
+        wait_vm<L::kLoads / NW + 1>();
+    else
+        wait_vm<L::kLoads / NW>();
 }
 
 // Combine a value with the one held by the lane 32 apart (the other half of
@@ -284,7 +334,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // 1's after it, each fragment read four products ahead; block 0's mask and
 // max run between block 1's products.  The order is fixed with scheduling
 // fences.
-template <bool kMask>
+template <class L, bool kMask>
 __device__ __forceinline__ float qk_tile_max(const bf16x8 (&qf)[8], const char* sK, int lane, int64_t key0,
                                              int64_t pos, f32x16& s0, f32x16& s1) {
     const int h = lane >> 5;
@@ -293,7 +343,7 @@ __device__ __forceinline__ float qk_tile_max(const bf16x8 (&qf)[8], const char* 
     s1 = zero16();
     bf16x8 kf[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kf[i] = k_frag(sK, 0, i, lane);
+    for (int i = 0; i < 4; ++i) kf[i] = L::k_frag(sK, 0, i, lane);
     float c0 = 0.0f, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -301,7 +351,7 @@ __device__ __forceinline__ float qk_tile_max(const bf16x8 (&qf)[8], const char* 
             s0 = mfma(kf[i & 3], qf[i & 7], s0);
         else
             s1 = mfma(kf[i & 3], qf[i & 7], s1);
-        if (i + 4 < 16) kf[i & 3] = k_frag(sK, (i + 4) >> 3, (i + 4) & 7, lane);
+        if (i + 4 < 16) kf[i & 3] = L::k_frag(sK, (i + 4) >> 3, (i + 4) & 7, lane);
         if (i == 9) {
             if (kMask) {
 #pragma unroll
@@ -364,12 +414,12 @@ __device__ __forceinline__ void p_step(const f32x16& s, int u, float c, float nm
 }
 
 // o += P V for one 16-key step (kb, u) over the wave's NDB d blocks.
-template <int NDB>
+template <class L, int NDB>
 __device__ __forceinline__ void pv_step(const bf16x8& pf, const char* sV, int kb, int u, int lane, f32x16 (&o)[NDB],
                                         int dblk0) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-        const bf16x8 vf = vt_frag(sV, kb, u, dblk0 + db, lane);
+        const bf16x8 vf = L::vt_frag(sV, kb, u, dblk0 + db, lane);
         o[db] = mfma(vf, pf, o[db]);
     }
 }
@@ -382,12 +432,12 @@ __device__ __forceinline__ void pv_step(const bf16x8& pf, const char* sV, int kb
 // its reference max always moves and a = 0, and o * 0 = +0 = o, so the
 // rescale is skipped and the products start from a zero accumulator -- the
 // same bits as the general form.
-template <int NDB, bool kMask, bool kFirst = false>
+template <class L, int NDB, bool kMask, bool kFirst = false>
 __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
                                           int64_t key0, int64_t pos, float c, float& mc, float& l,
                                           f32x16 (&o)[NDB], int dblk0) {
     f32x16 s0, s1;
-    float mt = qk_tile_max<kMask>(qf, sK, lane, key0, pos, s0, s1);
+    float mt = qk_tile_max<L, kMask>(qf, sK, lane, key0, pos, s0, s1);
     {
         float lo, hi;
         halves(mt, lo, hi);
@@ -409,13 +459,13 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
     } else {
         rescale_o<NDB>(o, a, any_grow);
     }
-    pv_step<NDB>(pf[0][0], sV, 0, 0, lane, o, dblk0);
+    pv_step<L, NDB>(pf[0][0], sV, 0, 0, lane, o, dblk0);
     p_step(s0, 1, c, nmc, pf[0][1], acc);
-    pv_step<NDB>(pf[0][1], sV, 0, 1, lane, o, dblk0);
+    pv_step<L, NDB>(pf[0][1], sV, 0, 1, lane, o, dblk0);
     p_step(s1, 0, c, nmc, pf[1][0], acc);
-    pv_step<NDB>(pf[1][0], sV, 1, 0, lane, o, dblk0);
+    pv_step<L, NDB>(pf[1][0], sV, 1, 0, lane, o, dblk0);
     p_step(s1, 1, c, nmc, pf[1][1], acc);
-    pv_step<NDB>(pf[1][1], sV, 1, 1, lane, o, dblk0);
+    pv_step<L, NDB>(pf[1][1], sV, 1, 1, lane, o, dblk0);
 
     // the two lane halves of the column: (low + high)
     float ls_lo, ls_hi;
