@@ -503,22 +503,33 @@ __device__ __forceinline__ void combine_row(const float* ws_o, const float* ws_m
     float Mc = ws_ml[base * 2 + 0];
     float L = ws_ml[base * 2 + 1];
     float O = ws_o[base * kHeadDim + d];
-    for (int k = 1; k < n_chunks; ++k) {
-        const float mc = ws_ml[(base + k) * 2 + 0];
-        const float l = ws_ml[(base + k) * 2 + 1];
-        const float o = ws_o[(base + k) * kHeadDim + d];
-        float Mcn, A, B;
-        fold_scalars(Mc, mc, Mcn, A, B);
-        L = __builtin_fmaf(L, A, l * B);
-        O = fold_value(O, A, o, B);
-        Mc = Mcn;
+    // partials are loaded kBatch chunks at a time, then folded one by one in
+    // chunk order, so the loads of a batch are in flight together
+    constexpr int kBatch = 8;
+    for (int k0 = 1; k0 < n_chunks; k0 += kBatch) {
+        float mcs[kBatch], ls[kBatch], os[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int64_t r = base + min(k0 + i, n_chunks - 1);
+            mcs[i] = ws_ml[r * 2 + 0];
+            ls[i] = ws_ml[r * 2 + 1];
+            os[i] = ws_o[r * kHeadDim + d];
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (k0 + i < n_chunks) {
+                float Mcn, A, B;
+                fold_scalars(Mc, mcs[i], Mcn, A, B);
+                L = __builtin_fmaf(L, A, ls[i] * B);
+                O = fold_value(O, A, os[i], B);
+                Mc = Mcn;
+            }
+        }
     }
     orow[d] = finalize(O, L);
     if (lse_row && d == 0) *lse_row = lse_of(Mc, L);
 }
 
-// One workgroup per (batch, query head): copy chunk 0, fold chunks 1.. in
-// order, finalize.
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     const int64_t row = blockIdx.x;
     // the row's chunks: those up to the one holding its position
