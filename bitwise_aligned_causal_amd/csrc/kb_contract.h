@@ -28,7 +28,7 @@
 //   per chunk, in chunk order (first chunk is copied, the rest folded):
 //     Mc' = max(Mc, mc); A = (Mc' == Mc) ? 1 : exp2(Mc - Mc')
 //     B   = (Mc' == mc) ? 1 : exp2(mc - Mc'); L = fma(L, A, l B); O = fma(O, A, o B)
-//   out = bf16_rne(O / L)  (IEEE division)
+//   out = bf16_rne(q), q = O / L by reciprocal and one correction (finalize)
 //   lse = (Mc + log2(L)) * fp32(ln 2)   (v_log_f32; natural-log log-sum-exp
 //         of the scaled scores, emitted on request from the same (Mc, L))
 //
@@ -446,8 +446,10 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
     const float mtc = mt * c;
     const bool grow = (mtc - mc) > kLazyTau;
     const float mcn = grow ? mtc : mc;
-    const float a = grow ? exp2_hw(mc - mcn) : 1.0f;
     const bool any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
+    // a = 1 for every column unless one of the wave's columns moved
+    float a = 1.0f;
+    if (any_grow) a = grow ? exp2_hw(mc - mcn) : 1.0f;
     const float nmc = -mcn;
 
     bf16x8 pf[2][2];
@@ -487,9 +489,19 @@ __device__ __forceinline__ float fold_value(float O, float A, float o, float B) 
     return __builtin_fmaf(O, A, o * B);
 }
 
+// out = bf16_rne(q) with q = O / L by Markstein's reciprocal-and-correction
+// sequence: y = rcp(L) refined by one Newton step, q0 = O y, r = O - q0 L
+// (exact, one fma), q = q0 + r y.  It costs a few instructions instead of a
+// full IEEE division per element (y is the same for a row, so it is computed
+// once); every kernel uses this same sequence.  L >= 1 (the key that set the
+// reference max contributes 2^0), so no step meets a denormal or infinity.
 __device__ __forceinline__ uint16_t finalize(float O, float L) {
-    const __bf16 r = (__bf16)(O / L);
-    return __builtin_bit_cast(uint16_t, r);
+    float y = __builtin_amdgcn_rcpf(L);
+    y = __builtin_fmaf(__builtin_fmaf(-L, y, 1.0f), y, y);
+    const float q0 = O * y;
+    const float r = __builtin_fmaf(-q0, L, O);
+    const __bf16 q = (__bf16)__builtin_fmaf(r, y, q0);
+    return __builtin_bit_cast(uint16_t, q);
 }
 
 // Natural-log log-sum-exp of a row from its final (Mc, L): Mc + log2(L) is
