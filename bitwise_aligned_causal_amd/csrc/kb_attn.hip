@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <initializer_list>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -295,22 +296,12 @@ constexpr int kDecodeWaves = 4;
 // query rows per head a decode workgroup can carry: 4 heads x 8 rows fill the
 // 32 columns of one MFMA block
 constexpr int kDecodeMaxRows = 8;
-// Two stages (64 KiB of LDS) let two decode workgroups share a CU; measured
-// on B=16, L=8192 this streams faster than one workgroup with a deeper ring.
-constexpr int kDecodeStages = 2;
-
-// Wait until at most `ahead` tiles of this wave's decode loads are pending.
-__device__ __forceinline__ void wait_tiles_decode(int ahead) {
-    constexpr int per = SwizzledTile::kLoads / kDecodeWaves;
-    static_assert(SwizzledTile::kLoads % kDecodeWaves == 0, "every wave issues the same loads");
-    switch (ahead) {
-        case 0: wait_vm<0>(); break;
-        case 1: wait_vm<per>(); break;
-        case 2: wait_vm<2 * per>(); break;
-        case 3: wait_vm<3 * per>(); break;
-        default: wait_vm<4 * per>(); break;
-    }
-}
+// K and V are loaded kDecodeLead iterations before they are read
+// (decode_body); the rings take 2 (kDecodeLead + 1) x 16 KiB of LDS.  With
+// one iteration of lead (64 KiB) two workgroups share a CU; deeper leads
+// (96 and 128 KiB, one workgroup per CU) measured slower at every batch.
+constexpr int kDecodeLead = 1;
+constexpr int kDecodeLdsBytes = 2 * (kDecodeLead + 1) * SwizzledTile::kKStage;
 
 // Everything a decode workgroup needs once its work item is known.
 struct DecodeWork {
@@ -336,11 +327,13 @@ struct DecodeWork {
 // Workgroup = 4 waves on one (sequence, KV head, chunk).  The four query heads
 // sit in MFMA columns 0..3 (the other columns hold zeros).  Every wave computes
 // the scores of the tile; wave w accumulates the output rows d = 32w..32w+31.
-// The chunk's tiles stream through a kDecodeStages-deep LDS ring.  With kPaged
+// The chunk's tiles stream through LDS rings of K and V, and the scores of
+// tile t + 1 are computed beside the softmax and P V of tile t (the same
+// operations as tile_step, so the bits of the prefill).  With kPaged
 // the keys come from a paged cache: a page holds page_size (a multiple of 64)
 // consecutive keys, so every 64-key tile lies inside one page; page indices
 // are clamped to the pool, so no table entry can make a load leave it.
-template <bool kPaged>
+template <bool kPaged, int kLead>
 __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, float* ws_ml, float c, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -374,23 +367,59 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
         pg = lane <= p1 - p0 ? wk.pages[p0 + lane] : 0;
         pg = min(max(pg, 0), wk.n_pages - 1);
     }
-    auto stage = [&](int t, char* nb) {
+    // K and V stream through separate rings of kLead + 1 stages of 16 KiB:
+    // the scores of tile t + 1 read K(t + 1) while the P V products of tile t
+    // read V(t).  Iteration t starts, after a barrier, the pair
+    // (K(t + kLead + 1), V(t + kLead)) into the stages of K(t) and V(t - 1),
+    // which every wave has finished with; the pair is needed kLead
+    // iterations later.
+    constexpr int kKStages = kLead + 1, kVStages = kLead + 1;
+    char* const kring = smem;
+    char* const vring = smem + kKStages * SwizzledTile::kKStage;
+    auto kst = [&](int t) { return kring + (t % kKStages) * SwizzledTile::kKStage; };
+    auto vst = [&](int t) { return vring + (t % kVStages) * SwizzledTile::kKStage; };
+    auto tile_base = [&](int t, const uint16_t* pool, const uint16_t* dense, int64_t& key0, int64_t& len) {
+        key0 = (int64_t)t * kTile;
+        len = kv_len;
         if (kPaged) {
-            const int64_t key0 = (int64_t)t * kTile;
             const int page = __builtin_amdgcn_readlane(pg, (int)(key0 / wk.page_size) - p0);
             const int64_t off = (int64_t)page * wk.page_elems + wk.head_elems + (key0 % wk.page_size) * kHeadDim;
-            stage_tile(plan, wk.kpool + off, wk.vpool + off, 0, min((int64_t)kTile, kv_len - key0), nb,
-                       lane, w);
-        } else {
-            stage_tile(plan, kbase, vbase, (int64_t)t * kTile, kv_len, nb, lane, w);
+            len = min((int64_t)kTile, kv_len - key0);
+            key0 = 0;
+            return pool + off;
+        }
+        return dense;
+    };
+    auto load_k = [&](int t) {
+        int64_t key0, len;
+        const uint16_t* base = tile_base(t, wk.kpool, kbase, key0, len);
+        stage_half<SwizzledTile, kDecodeWaves, false>(plan, base, key0, len, kst(t), lane, w);
+    };
+    auto load_v = [&](int t) {
+        int64_t key0, len;
+        const uint16_t* base = tile_base(t, wk.vpool, vbase, key0, len);
+        stage_half<SwizzledTile, kDecodeWaves, true>(plan, base, key0, len, vst(t), lane, w);
+    };
+    // the pair of iteration s (s < t0: issued before the loop)
+    constexpr int kHalfLoads = SwizzledTile::kKLoads / kDecodeWaves;  // per wave and half tile
+    auto pair_loads = [&](int s) { return (s + kLead + 1 < t1 ? kHalfLoads : 0) + (s + kLead < t1 ? kHalfLoads : 0); };
+    auto issue_pair = [&](int s) {
+        if (s + kLead + 1 < t1) load_k(s + kLead + 1);
+        if (s + kLead < t1) load_v(s + kLead);
+    };
+    // wait until at most `allow` of this wave's loads are pending
+    auto wait_allow = [&](int allow) {
+        switch (allow / kHalfLoads) {
+            case 0: wait_vm<0>(); break;
+            case 1: wait_vm<kHalfLoads>(); break;
+            case 2: wait_vm<2 * kHalfLoads>(); break;
+            case 3: wait_vm<3 * kHalfLoads>(); break;
+            case 4: wait_vm<4 * kHalfLoads>(); break;
+            case 5: wait_vm<5 * kHalfLoads>(); break;
+            default: wait_vm<6 * kHalfLoads>(); break;
         }
     };
-
-    // ring of kDecodeStages tiles, loads kDecodeStages - 1 tiles ahead
-#pragma unroll
-    for (int i = 0; i < kDecodeStages - 1; ++i) {
-        if (t0 + i < t1) stage(t0 + i, smem + i * SwizzledTile::kBytes);
-    }
+    static_assert(kLead >= 1 && kLead <= 4, "wait_allow covers the loads of up to three pairs");
 
     const int64_t qrow_idx = wk.q_row0 + (int64_t)hi * wk.q_hstride + ri;
     bf16x8 qf[8];
@@ -404,27 +433,43 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
         }
     }
 
+    // Q first, then K(t0) and the pairs of iterations t0 - kLead .. t0 - 1
+    load_k(t0);
+    for (int s = t0 - kLead; s < t0; ++s) issue_pair(s);
     float mc = -__builtin_inff(), l = 0.0f;  // max in log2 units
     f32x16 acc[1];
     acc[0] = zero16();
-    for (int t = t0; t < t1; ++t) {
-        // tiles issued after tile t and still allowed in flight
-        const int ahead = min(t1 - 1, t + kDecodeStages - 2) - t;
-        wait_tiles_decode(ahead);
+    // (the first use of the Q fragments waits for every load issued so far)
+    wait_vm<0>();
+    __syncthreads();
+    f32x16 s0, s1;
+    qk_plain<SwizzledTile>(qf, kst(t0), lane, s0, s1);
+    // Tiles from t_mask on hold keys beyond the first row's position (only
+    // the context's last tile when n_rows = 1) and take the masked softmax.
+    // The scores of tile t + 1 are computed in iteration t even past the
+    // chunk's end (from a stale or unwritten stage; never used), which keeps
+    // each iteration one straight block.
+    const int64_t full = kv_len - n_rows - (kTile - 1);  // tile t is unmasked iff 64 t <= full and t < n_tiles - 1
+    const int t_mask = full < 0 ? 0 : min(n_tiles - 1, (int)(full / kTile) + 1);
+    auto iteration = [&](int t, auto masked) {
+        // K(t + 1) and V(t) came with the pair of iteration t - kLead; the
+        // pairs of the iterations after it may still be in flight
+        int allow = 0;
+        for (int s = t - kLead + 1; s < t; ++s) allow += pair_loads(s);
+        wait_allow(allow);
         __syncthreads();
-        if (t + kDecodeStages - 1 < t1)
-            stage(t + kDecodeStages - 1,
-                  smem + ((t + kDecodeStages - 1 - t0) % kDecodeStages) * SwizzledTile::kBytes);
-        const char* buf = smem + ((t - t0) % kDecodeStages) * SwizzledTile::kBytes;
-        // a tile needs the mask when it holds keys beyond the first row's
-        // position (only the context's last tile when n_rows = 1)
-        if (t < n_tiles - 1 && (int64_t)t * kTile + kTile - 1 <= kv_len - n_rows)
-            tile_step<SwizzledTile, 1, false>(qf, buf, buf + SwizzledTile::kKStage, lane, (int64_t)t * kTile, pos, c, mc,
-                                              l, acc, w);
-        else
-            tile_step<SwizzledTile, 1, true>(qf, buf, buf + SwizzledTile::kKStage, lane, (int64_t)t * kTile, pos, c, mc,
-                                             l, acc, w);
-    }
+        issue_pair(t);
+        bf16x8 pf[2][2];
+        softmax_flat<1, decltype(masked)::value>(s0, s1, lane, (int64_t)t * kTile, pos, c, mc, l, acc, pf);
+        f32x16 n0, n1;
+        qk_plain<SwizzledTile>(qf, kst(t + 1), lane, n0, n1);
+        pv_plain<SwizzledTile, 1>(pf, vst(t), lane, acc, w);
+        s0 = n0;
+        s1 = n1;
+    };
+    int t = t0;
+    for (; t < min(t1, t_mask); ++t) iteration(t, std::false_type{});
+    for (; t < t1; ++t) iteration(t, std::true_type{});
 
     if (!active) return;
     if (wk.n_chunks == 1) {
@@ -461,7 +506,7 @@ __device__ __forceinline__ void decode_body(const DecodeWork& wk, float* ws_o, f
 
 // Dense batch: q, o [batch, Hq, 1, 128]; caches [batch, Hkv, cap, 128].
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * SwizzledTile::kBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kDecodeLdsBytes];
     const int x = blockIdx.x;
     const int chunk = x % a.n_chunks;
     const int bg = x / a.n_chunks;
@@ -481,7 +526,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     wk.chunk = chunk;
     wk.n_chunks = a.n_chunks;
     wk.ws_row0 = wk.q_row0 * a.n_chunks;
-    decode_body<false>(wk, a.ws_o, a.ws_ml, a.c, smem);
+    decode_body<false, kDecodeLead>(wk, a.ws_o, a.ws_ml, a.c, smem);
 }
 
 struct CombineArgs {
@@ -569,7 +614,7 @@ struct DecodeVarlenArgs {
 
 template <bool kPaged>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_varlen_kernel(DecodeVarlenArgs a, DecodeVarlenTable t) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDecodeStages * SwizzledTile::kBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kDecodeLdsBytes];
     const int x = blockIdx.x;
     int s = 0;
     while (s + 1 < t.n_seqs && t.unit0[s + 1] <= x) ++s;
@@ -601,7 +646,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_varlen_kernel(Decode
     wk.chunk = chunk;
     wk.n_chunks = nc;
     wk.ws_row0 = t.ws_row0[s] + (int64_t)kGroup * g * nc;
-    decode_body<kPaged>(wk, a.ws_o, a.ws_ml, a.c, smem);
+    decode_body<kPaged, kDecodeLead>(wk, a.ws_o, a.ws_ml, a.c, smem);
 }
 
 // One workgroup per (sequence with more than one chunk, query head).

@@ -250,6 +250,32 @@ __device__ __forceinline__ void stage_tile(const StagePlan<L, NW>& p, const uint
     }
 }
 
+// Issue this wave's loads of only the K half (kV = false) or only the V half
+// of the tile at key0 (from `base`, the K or the V tensor) into `dst`, that
+// half's own region of L::kKStage bytes; otherwise as stage_tile.
+template <class L, int NW, bool kV>
+__device__ __forceinline__ void stage_half(const StagePlan<L, NW>& p, const uint16_t* base, int64_t key0,
+                                           int64_t kv_len, char* dst, int lane, int wave) {
+    static_assert(L::kKLoads % NW == 0 && 2 * L::kKLoads == L::kLoads, "loads k < kN/2 fill K, the rest V");
+    constexpr int kHalf = StagePlan<L, NW>::kN / 2;
+    const char* tb = reinterpret_cast<const char*>(base + key0 * kHeadDim);
+    if (key0 + kTile <= kv_len) {
+#pragma unroll
+        for (int k = kV ? kHalf : 0; k < (kV ? 2 * kHalf : kHalf); ++k) {
+            const int i = wave + k * NW;
+            lds_dma16(tb, p.off[k], dst + 1024 * (i - (kV ? L::kKLoads : 0)));
+        }
+    } else {
+        for (int i = wave + (kV ? L::kKLoads : 0); i < (kV ? L::kLoads : L::kKLoads); i += NW) {
+            int row;
+            bool v;
+            const uint32_t off = L::src(i, lane, row, v);
+            const int64_t keep = key0 + row < kv_len ? 0 : (key0 + row - (kv_len - 1)) * 256;
+            lds_dma16_flat(tb + (off - keep), dst + 1024 * (i - (kV ? L::kKLoads : 0)));
+        }
+    }
+}
+
 // Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -475,6 +501,75 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
     const float ls = ls_lo + ls_hi;
     l = __builtin_fmaf(l, a, ls);
     mc = mcn;
+}
+
+// ---------------------------------------------------------------------------
+// tile_step in parts without branches, for the decode, which computes the
+// scores of tile t + 1 beside the softmax and P V of tile t: qk_plain issues
+// the score products (chains of both key blocks interleaved); softmax_flat
+// does the mask, max, lazy reference update, P, row sum and rescale of o as
+// tile_step does, but always computes a and always multiplies o by it (o * 1
+// == o exactly, so the bits are those of tile_step); pv_plain issues the P V
+// products in pv_step's order.
+// ---------------------------------------------------------------------------
+template <class L>
+__device__ __forceinline__ void qk_plain(const bf16x8 (&qf)[8], const char* sK, int lane, f32x16& s0, f32x16& s1) {
+    s0 = zero16();
+    s1 = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        s0 = mfma(L::k_frag(sK, 0, st, lane), qf[st], s0);
+        s1 = mfma(L::k_frag(sK, 1, st, lane), qf[st], s1);
+    }
+}
+
+template <int NDB, bool kMask>
+__device__ __forceinline__ void softmax_flat(f32x16& s0, f32x16& s1, int lane, int64_t key0, int64_t pos, float c,
+                                             float& mc, float& l, f32x16 (&o)[NDB], bf16x8 (&pf)[2][2]) {
+    if (kMask) {
+        const int h = lane >> 5;
+        const float ninf = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
+            s0[v] = kk > pos ? ninf : s0[v];
+            s1[v] = kk + 32 > pos ? ninf : s1[v];
+        }
+    }
+    float mt = vmax(block_max(s0), block_max(s1));
+    {
+        float lo, hi;
+        halves(mt, lo, hi);
+        mt = vmax(lo, hi);
+    }
+    const float mtc = mt * c;
+    const bool grow = (mtc - mc) > kLazyTau;
+    const float mcn = grow ? mtc : mc;
+    const float a = grow ? exp2_hw(mc - mcn) : 1.0f;
+    const float nmc = -mcn;
+    float acc = 0.0f;  // this lane's row-sum chain over the tile's 16 dot2 terms
+    p_step(s0, 0, c, nmc, pf[0][0], acc);
+    p_step(s0, 1, c, nmc, pf[0][1], acc);
+    p_step(s1, 0, c, nmc, pf[1][0], acc);
+    p_step(s1, 1, c, nmc, pf[1][1], acc);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] = o[db][v] * a;
+    }
+    float ls_lo, ls_hi;
+    halves(acc, ls_lo, ls_hi);
+    l = __builtin_fmaf(l, a, ls_lo + ls_hi);
+    mc = mcn;
+}
+
+template <class L, int NDB>
+__device__ __forceinline__ void pv_plain(const bf16x8 (&pf)[2][2], const char* sV, int lane, f32x16 (&o)[NDB],
+                                         int dblk0) {
+    pv_step<L, NDB>(pf[0][0], sV, 0, 0, lane, o, dblk0);
+    pv_step<L, NDB>(pf[0][1], sV, 0, 1, lane, o, dblk0);
+    pv_step<L, NDB>(pf[1][0], sV, 1, 0, lane, o, dblk0);
+    pv_step<L, NDB>(pf[1][1], sV, 1, 1, lane, o, dblk0);
 }
 
 // Fold weights of one chunk into the running total (scalars of one column,
