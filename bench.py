@@ -66,6 +66,17 @@ def source_hash(names) -> str:
     return h.hexdigest()[:16]
 
 
+def device_env(torch, dev) -> dict:
+    """The GPU and software the line was measured on."""
+    p = torch.cuda.get_device_properties(dev)
+    env = {"gpu": torch.cuda.get_device_name(dev), "arch": getattr(p, "gcnArchName", None),
+           "compute_units": p.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__}
+    clock = getattr(p, "clock_rate", None)
+    if clock:
+        env["clock_mhz"] = round(clock / 1000)
+    return env
+
+
 def kernel_source_hash() -> str:
     """Source hash of the forward kernels."""
     return source_hash(("kb_attn.hip", "kb_contract.h"))
@@ -448,6 +459,9 @@ def main() -> int:
         "bitwise_mismatch": {"partitioned_vs_prefill": mism, "decode_vs_prefill": mism_dec},
         "contract": kb.contract(),
         "kernel_source_hash": kernel_source_hash(),
+        "inputs_sha256": {name: hashlib.sha256(np.ascontiguousarray(x).data).hexdigest()[:16]
+                          for name, x in (("q", q), ("k", k), ("v", v))},
+        "env": device_env(torch, dev),
     }
     if not args.no_cpu_baseline:
         base, rows, ref = cpu_baseline(q, k, v, args.cpu_seconds)
