@@ -221,6 +221,28 @@ def test_constant_v(kb):
     assert np.abs(got - 1.5).max() <= 2.0 ** -7
 
 
+@pytest.mark.parametrize("scale", [1.0, 1e-3])
+def test_extreme_scales(kb, scale):
+    """A sharp softmax (scale 1: score spreads of hundreds of log2 units, so
+    reference-max moves, exponentials that underflow to zero and chunk folds
+    with a zero weight) and a nearly flat one (scale 1e-3: row sums close to
+    the context length): the three entry points agree bit for bit and the
+    prefill meets the oracle's tolerance on sampled rows."""
+    B, S, seed = 2, 2100, 4242
+    q, k, v = kb_gen.attention_inputs(seed, B, S)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    note(f"prefill B={B} S={S} scale={scale}")
+    pre = bits(kb.prefill(qd, kd, vd, scale=scale))
+    note(f"partitioned rows 1024.. and decode of the last row, scale={scale}")
+    part = bits(kb.partitioned(qd[:, :, 1024:].contiguous(), kd, vd, kv_len=S, scale=scale))
+    assert_same_bits(part, pre[:, :, 1024:], f"partitioned vs prefill, scale={scale}")
+    dec = bits(kb.decode(qd[:, :, -1:].contiguous(), kd, vd, scale=scale))
+    assert_same_bits(dec[:, :, 0], pre[:, :, -1], f"decode vs last prefill row, scale={scale}")
+    rows = sample_rows(np.random.default_rng(seed), B, HQ, S, extra=10)
+    ref = oracle.attention(q, k, v, scale=scale, rows=rows, threads=oracle_threads())
+    compare(pre.reshape(-1, D)[rows], ref, f"prefill scale={scale} sampled rows")
+
+
 def test_stale_workspace_does_not_matter(kb):
     import torch
 
