@@ -54,9 +54,14 @@ def prefill_flops(batch: int, n_rows_first_pos: int, n_rows: int) -> int:
 
 
 def source_hash(names) -> str:
-    """Hash of kernel sources with comments and whitespace removed, so that a
-    counter summary stays valid across edits that change no code."""
+    """Hash of kernel sources with comments and whitespace removed, and of the
+    compiler flags they are built with, so that a counter summary stays valid
+    across edits that change no code and lapses when the code or the flags
+    change."""
+    from bitwise_aligned_causal_amd import _build
+
     h = hashlib.sha256()
+    h.update(" ".join(_build.HIPCC_FLAGS).encode())
     for name in names:
         with open(os.path.join(ROOT, "bitwise_aligned_causal_amd", "csrc", name)) as fh:
             text = fh.read()

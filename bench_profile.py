@@ -106,7 +106,7 @@ def sq_summary(dirs, out: str, src_hash: str) -> None:
             vals.update(rows)
     tiles = prefill_wave_tiles()
     lines = [f"# prefill_kernel<false> SQ counters, B={bench.B} S={bench.S} ({tiles / 8:.3g} workgroup-tiles x 8 waves)",
-             f"kernel source hash (code without comments): {src_hash}", "",
+             f"kernel hash (code without comments, and compiler flags): {src_hash}", "",
              "commands (one pass each, counters split to stay within the SQ block limit):"]
     lines += [f"  rocprofv3 --pmc {p} -d <dir> -o run --output-format csv -- "
               "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras" for p in SQ_PASSES]
@@ -143,7 +143,7 @@ def write_summaries(kernels, stats, fetch, write, f_fetch, f_write, src_hash, ou
         avg_us = float(st["AverageNs"]) / 1e3
         lines = [
             f"# {k}: {what}",
-            f"kernel source hash (code without comments): {src_hash}",
+            f"kernel hash (code without comments, and compiler flags): {src_hash}",
             "",
             "commands:",
             f"  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- python3 bench.py {stats_args}",

@@ -22,6 +22,10 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA operands and results in ordinary vector registers: without it the
+    # decode kernels put 48 registers in the accumulation file and spend ~180
+    # copy instructions moving them back and forth
+    "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
 ]
 
 
