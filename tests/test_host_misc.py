@@ -44,3 +44,27 @@ def test_kernel_source_hash_is_stable():
 
     assert bench.kernel_source_hash() == bench.kernel_source_hash()
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_build_flags_that_the_kernels_rely_on():
+    """The contract places every fused multiply-add explicitly (no contraction),
+    packed fp32 arithmetic stays off, the code targets gfx950 only, and MFMA
+    operands stay in ordinary vector registers."""
+    from bitwise_aligned_causal_amd import _build
+
+    flags = _build.HIPCC_FLAGS
+    assert "-ffp-contract=off" in flags
+    i = flags.index("-packed-fp32-ops")
+    assert flags[i - 3:i] == ["-Xclang", "-target-feature", "-Xclang"]
+    assert [f for f in flags if f.startswith("--offload-arch")] == ["--offload-arch=gfx950"]
+    assert "-mllvm=-amdgpu-mfma-vgpr-form" in flags
+
+
+def test_kernel_hash_covers_the_build_flags(monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    from bitwise_aligned_causal_amd import _build
+
+    before = bench.kernel_source_hash()
+    monkeypatch.setattr(_build, "HIPCC_FLAGS", _build.HIPCC_FLAGS + ["-DKB_EXTRA"])
+    assert bench.kernel_source_hash() != before
