@@ -31,6 +31,10 @@
  *   - head_dim must be 128 and n_q_heads must equal 4 * n_kv_heads.
  *   - scale multiplies <q, k>; it must be finite and > 0 (1/sqrt(128) in the
  *     README's workloads, whose API takes no scale).
+ *   - q, k and v must hold finite values.  Scores are accumulated in fp32, so
+ *     a row whose scale * <q, k_j> leaves the fp32 range (about 3.4e38) is
+ *     outside the contract and its output is not specified; the library does
+ *     not check the values (that would cost a pass over the cache).
  *   - The caller owns every buffer; the library allocates nothing, keeps no
  *     state and is thread-safe.  Calls are asynchronous on `stream` (0 = the
  *     null stream) and return once the work is enqueued.
