@@ -18,8 +18,8 @@
 //     s_j   = MFMA chain over d in k-steps 0..7 (step st covers d 16st..16st+15)
 //     s_j   = -inf where key j > pos                  (select)
 //     mtc   = (max_j s_j) * c                         with c = fp32(scale * log2 e)
-//     grow  = mtc - mc > 32;  mc' = grow ? mtc : mc;  a = grow ? exp2(mc - mc') : 1
-//     p_j   = exp2(fma(s_j, c, -mc'));  P_j = bf16_rne(p_j)   (P_j <= 2^32)
+//     grow  = mtc - mc > 64;  mc' = grow ? mtc : mc;  a = grow ? exp2(mc - mc') : 1
+//     p_j   = exp2(fma(s_j, c, -mc'));  P_j = bf16_rne(p_j)   (P_j <= 2^64)
 //     l     = fma(l, a, sum(P))   sum: per lane half, one chain of 16 bf16
 //             dot2 with (1, 1) over the key steps (0,0), (0,1), (1,0), (1,1)
 //             in order, 4 per step; then (low half + high half)
@@ -344,13 +344,13 @@ __device__ __forceinline__ f32x16 zero16() {
 //   o[db]   : O^T accumulators for d rows 32*(dblk0+db) .. +31 of column j
 // ---------------------------------------------------------------------------
 // The reference max moves only when a tile's max exceeds it by more than
-// kLazyTau (log2 units), so P <= 2^32, a chunk's row sum <= 2^42 and its
-// accumulators <= 2^42 max|v|, all far inside the fp32 / bf16 range; relative
-// rounding does not depend on the scale.  A high threshold makes the O rescale
-// rare: on queries and keys with strong outlier channels (score spread of
-// about 16 log2 units) a threshold of 8 rescales on about 2 tiles in 3, this
-// one on about 1 in 6 (mostly the first tile of a chunk).
-constexpr float kLazyTau = 32.0f;
+// kLazyTau (log2 units), so P <= 2^64, a chunk's row sum <= 2^74 and its
+// accumulators <= 2^74 max|v|, inside the fp32 / bf16 range for |v| < 2^54;
+// relative rounding does not depend on the scale.  A high threshold makes the
+// O rescale rare: on queries and keys with strong outlier channels (score
+// spread of about 16 log2 units) a threshold of 8 rescales on about 2 tiles in
+// 3, 32 on about 1 in 6 (mostly the first tile of a chunk, which skips it).
+constexpr float kLazyTau = 64.0f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));

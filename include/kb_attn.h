@@ -56,7 +56,7 @@ extern "C" {
 
 #define KB_ATTN_KV_TILE 64
 #define KB_ATTN_KV_CHUNK 1024
-#define KB_ATTN_CONTRACT_VERSION 5
+#define KB_ATTN_CONTRACT_VERSION 6
 
 enum {
     KB_ATTN_OK = 0,
