@@ -149,6 +149,25 @@ def _check_tensor(name, x, ndim=4):
                          f"(got {x.dtype}, {x.device}, shape {tuple(x.shape)})")
 
 
+def _check_like(name, x, like, ndim=4):
+    """x is a contiguous bf16 GPU tensor with exactly the shape and device of
+    `like`: the library takes only a pointer for an output, so a smaller
+    buffer would be written past its end."""
+    _check_tensor(name, x, ndim)
+    if tuple(x.shape) != tuple(like.shape) or x.device != like.device:
+        raise ValueError(f"{name} must have shape {tuple(like.shape)} on {like.device} "
+                         f"(got {tuple(x.shape)} on {x.device})")
+
+
+def _same_device(*named):
+    """Every tensor on the device of the first (the library checks residency on
+    the current device, the binding that they agree with each other)."""
+    dev = named[0][1].device
+    for n, x in named[1:]:
+        if x.device != dev:
+            raise ValueError(f"{n} is on {x.device}, {named[0][0]} on {dev}")
+
+
 def _stream(x):
     return ctypes.c_void_p(_torch().cuda.current_stream(x.device).cuda_stream)
 
@@ -161,11 +180,12 @@ def prefill(q, k, v, scale: float | None = None, out=None):
     """Causal full-sequence forward: q [B, Hq, S, 128], k/v [B, Hkv, S, 128]."""
     for n, x in (("q", q), ("k", k), ("v", v)):
         _check_tensor(n, x)
+    _same_device(("q", q), ("k", k), ("v", v))
     B, Hq, S, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
         raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     out = _torch().empty_like(q) if out is None else out
-    _check_tensor("out", out)
+    _check_like("out", out, q)
     check(lib().kb_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, Hq,
                                 k.shape[1], D, _scale(scale, D), _stream(q)))
     return out
@@ -176,11 +196,12 @@ def partitioned(q, k_cache, v_cache, kv_len: int, scale: float | None = None, ou
     caches [B, Hkv, capacity, 128] holding kv_len keys."""
     for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_tensor(n, x)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache))
     B, Hq, q_len, D = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
         raise ValueError("cache shape mismatch")
     out = _torch().empty_like(q) if out is None else out
-    _check_tensor("out", out)
+    _check_like("out", out, q)
     check(lib().kb_attn_partitioned(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B,
                                     q_len, int(kv_len), k_cache.shape[2], Hq, k_cache.shape[1], D,
                                     _scale(scale, D), _stream(q)))
@@ -193,6 +214,7 @@ def decode(q, k_cache, v_cache, kv_len: int | None = None, scale: float | None =
     torch = _torch()
     for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_tensor(n, x)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache))
     B, Hq, one, D = q.shape
     if one != 1:
         raise ValueError("decode takes one query token per sequence")
@@ -205,7 +227,7 @@ def decode(q, k_cache, v_cache, kv_len: int | None = None, scale: float | None =
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     out = torch.empty_like(q) if out is None else out
-    _check_tensor("out", out)
+    _check_like("out", out, q)
     check(lib().kb_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B, kv_len,
                                k_cache.shape[2], Hq, k_cache.shape[1], D, _scale(scale, D), ws_ptr, ws_bytes,
                                _stream(q)))
@@ -224,6 +246,7 @@ def decode_multi(q, k_cache, v_cache, kv_len: int | None = None, scale: float | 
     torch = _torch()
     for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_tensor(n, x)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache))
     B, Hq, n_rows, D = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
         raise ValueError("cache shape mismatch")
@@ -234,7 +257,7 @@ def decode_multi(q, k_cache, v_cache, kv_len: int | None = None, scale: float | 
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     out = torch.empty_like(q) if out is None else out
-    _check_tensor("out", out)
+    _check_like("out", out, q)
     check(lib().kb_attn_decode_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B, n_rows,
                                      kv_len, k_cache.shape[2], Hq, k_cache.shape[1], D, _scale(scale, D), ws_ptr,
                                      ws_bytes, _stream(q)))
@@ -253,13 +276,14 @@ def prefill_varlen(q, k, v, cu_seqlens, scale: float | None = None, out=None):
     (host list of batch + 1 offsets, T = cu_seqlens[-1])."""
     for n, x in (("q", q), ("k", k), ("v", v)):
         _check_packed(n, x)
+    _same_device(("q", q), ("k", k), ("v", v))
     if k.shape != v.shape or k.shape[1] != q.shape[1]:
         raise ValueError("k/v must be [Hkv, T, 128] with the rows of q")
     cu = _host_i64(cu_seqlens)
     if int(cu_seqlens[-1]) != q.shape[1]:
         raise ValueError("cu_seqlens[-1] must equal the packed row count")
     out = _torch().empty_like(q) if out is None else out
-    _check_packed("out", out)
+    _check_like("out", out, q, ndim=3)
     check(lib().kb_attn_prefill_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu,
                                        len(cu_seqlens) - 1, q.shape[0], k.shape[0], HEAD_DIM,
                                        _scale(scale, HEAD_DIM), _stream(q)))
@@ -273,6 +297,7 @@ def partitioned_varlen(q, k_cache, v_cache, cu_q, cu_cache, kv_lens, scale: floa
     range cu_cache[i] .. cu_cache[i+1] - 1 (host lists)."""
     for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_packed(n, x)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache))
     if k_cache.shape != v_cache.shape:
         raise ValueError("cache shape mismatch")
     if int(cu_q[-1]) != q.shape[1] or int(cu_cache[-1]) != k_cache.shape[1]:
@@ -282,7 +307,7 @@ def partitioned_varlen(q, k_cache, v_cache, cu_q, cu_cache, kv_lens, scale: floa
         raise ValueError("cu_q, cu_cache and kv_lens describe different batch sizes")
     a_q, a_c, a_l = _host_i64(cu_q), _host_i64(cu_cache), _host_i64(kv_lens)
     out = _torch().empty_like(q) if out is None else out
-    _check_packed("out", out)
+    _check_like("out", out, q, ndim=3)
     check(lib().kb_attn_partitioned_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                                            a_q, a_c, a_l, batch, q.shape[0], k_cache.shape[0], HEAD_DIM,
                                            _scale(scale, HEAD_DIM), _stream(q)))
@@ -295,6 +320,7 @@ def decode_varlen(q, k_cache, v_cache, cu_cache, kv_lens, scale: float | None = 
     torch = _torch()
     for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_packed(n, x)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache))
     batch = q.shape[1]
     if len(cu_cache) != batch + 1 or len(kv_lens) != batch or int(cu_cache[-1]) != k_cache.shape[1]:
         raise ValueError("cu_cache / kv_lens do not match q and the caches")
@@ -305,7 +331,7 @@ def decode_varlen(q, k_cache, v_cache, cu_cache, kv_lens, scale: float | None = 
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a_c, a_l = _host_i64(cu_cache), _host_i64(kv_lens)
     out = torch.empty_like(q) if out is None else out
-    _check_packed("out", out)
+    _check_like("out", out, q, ndim=3)
     check(lib().kb_attn_decode_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), a_c,
                                       a_l, batch, q.shape[0], k_cache.shape[0], HEAD_DIM, _scale(scale, HEAD_DIM),
                                       ws_ptr, ws_bytes, _stream(q)))
@@ -326,6 +352,7 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float | None 
     if (not isinstance(block_table, torch.Tensor) or block_table.dtype != torch.int32 or not block_table.is_cuda
             or block_table.dim() != 2 or not block_table.is_contiguous() or block_table.shape[0] != q.shape[0]):
         raise ValueError("block_table must be a contiguous int32 [B, max_pages] tensor on the GPU")
+    _same_device(("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table))
     B, Hq = q.shape[0], q.shape[1]
     if len(kv_lens) != B:
         raise ValueError("kv_lens must have one entry per sequence")
@@ -336,7 +363,7 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float | None 
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a_l = _host_i64(kv_lens)
     out = torch.empty_like(q) if out is None else out
-    _check_tensor("out", out, ndim=3)
+    _check_like("out", out, q, ndim=3)
     check(lib().kb_attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
                                      block_table.data_ptr(), block_table.shape[1], a_l, B, k_pages.shape[0],
                                      k_pages.shape[2], Hq, k_pages.shape[1], HEAD_DIM, _scale(scale, HEAD_DIM), ws_ptr,
@@ -354,15 +381,23 @@ def _lse_out(lse, shape, like):
     return lse
 
 
+def _check_lse_in(lse, shape, layout):
+    torch = _torch()
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda
+            or tuple(lse.shape) != tuple(shape) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be the contiguous float32 {layout} GPU tensor of the forward")
+
+
 def prefill_lse(q, k, v, scale: float | None = None, out=None, lse=None):
     """prefill() that also returns the fp32 log-sum-exp of every row, [B, Hq, S]."""
     for n, x in (("q", q), ("k", k), ("v", v)):
         _check_tensor(n, x)
+    _same_device(("q", q), ("k", k), ("v", v))
     B, Hq, S, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
         raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     out = _torch().empty_like(q) if out is None else out
-    _check_tensor("out", out)
+    _check_like("out", out, q)
     lse = _lse_out(lse, (B, Hq, S), q)
     check(lib().kb_attn_prefill_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, S,
                                     Hq, k.shape[1], D, _scale(scale, D), _stream(q)))
@@ -373,11 +408,12 @@ def partitioned_lse(q, k_cache, v_cache, kv_len: int, scale: float | None = None
     """partitioned() that also returns the fp32 log-sum-exp of every row, [B, Hq, q_len]."""
     for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_tensor(n, x)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache))
     B, Hq, q_len, D = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
         raise ValueError("cache shape mismatch")
     out = _torch().empty_like(q) if out is None else out
-    _check_tensor("out", out)
+    _check_like("out", out, q)
     lse = _lse_out(lse, (B, Hq, q_len), q)
     check(lib().kb_attn_partitioned_lse(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                                         lse.data_ptr(), B, q_len, int(kv_len), k_cache.shape[2], Hq,
@@ -391,6 +427,7 @@ def decode_lse(q, k_cache, v_cache, kv_len: int | None = None, scale: float | No
     torch = _torch()
     for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_tensor(n, x)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache))
     B, Hq, one, D = q.shape
     if one != 1:
         raise ValueError("decode takes one query token per sequence")
@@ -403,7 +440,7 @@ def decode_lse(q, k_cache, v_cache, kv_len: int | None = None, scale: float | No
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     out = torch.empty_like(q) if out is None else out
-    _check_tensor("out", out)
+    _check_like("out", out, q)
     lse = _lse_out(lse, (B, Hq, 1), q)
     check(lib().kb_attn_decode_lse(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                                    lse.data_ptr(), B, kv_len, k_cache.shape[2], Hq, k_cache.shape[1], D,
@@ -421,19 +458,18 @@ def backward(q, k, v, out, dout, lse, scale: float | None = None, dq=None, dk=No
     torch = _torch()
     for n, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check_tensor(n, x)
+    _same_device(("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout))
     B, Hq, S, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
         raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     if out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("out and dout must be shaped like q")
-    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda
-            or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous()):
-        raise ValueError("lse must be the contiguous float32 [B, Hq, S] tensor of the forward")
+    _check_lse_in(lse, (B, Hq, S), "[B, Hq, S]")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_tensor(n, x)
+    for n, x, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_like(n, x, like)
     need = backward_workspace_bytes(B, S, Hq, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -448,13 +484,14 @@ def prefill_varlen_lse(q, k, v, cu_seqlens, scale: float | None = None, out=None
     """prefill_varlen() that also returns the fp32 log-sum-exp of every row, [Hq, T]."""
     for n, x in (("q", q), ("k", k), ("v", v)):
         _check_packed(n, x)
+    _same_device(("q", q), ("k", k), ("v", v))
     if k.shape != v.shape or k.shape[1] != q.shape[1]:
         raise ValueError("k/v must be [Hkv, T, 128] with the rows of q")
     if int(cu_seqlens[-1]) != q.shape[1]:
         raise ValueError("cu_seqlens[-1] must equal the packed row count")
     cu = _host_i64(cu_seqlens)
     out = _torch().empty_like(q) if out is None else out
-    _check_packed("out", out)
+    _check_like("out", out, q, ndim=3)
     lse = _lse_out(lse, (q.shape[0], q.shape[1]), q)
     check(lib().kb_attn_prefill_varlen_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                            cu, len(cu_seqlens) - 1, q.shape[0], k.shape[0], HEAD_DIM,
@@ -475,19 +512,18 @@ def backward_varlen(q, k, v, out, dout, lse, cu_seqlens, scale: float | None = N
     torch = _torch()
     for n, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _check_packed(n, x)
+    _same_device(("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout))
     T = q.shape[1]
     if k.shape != v.shape or k.shape[1] != T or out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("packed shapes do not match")
     if int(cu_seqlens[-1]) != T:
         raise ValueError("cu_seqlens[-1] must equal the packed row count")
-    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda
-            or tuple(lse.shape) != (q.shape[0], T) or not lse.is_contiguous()):
-        raise ValueError("lse must be the contiguous float32 [Hq, T] tensor of the forward")
+    _check_lse_in(lse, (q.shape[0], T), "[Hq, T]")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_packed(n, x)
+    for n, x, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_like(n, x, like, ndim=3)
     need = backward_varlen_workspace_bytes(cu_seqlens, q.shape[0])
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

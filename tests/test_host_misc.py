@@ -68,3 +68,103 @@ def test_kernel_hash_covers_the_build_flags(monkeypatch):
     before = bench.kernel_source_hash()
     monkeypatch.setattr(_build, "HIPCC_FLAGS", _build.HIPCC_FLAGS + ["-DKB_EXTRA"])
     assert bench.kernel_source_hash() != before
+
+
+class _FakeLib:
+    """Stands in for libkb_attn.so: workspace queries answer 64 bytes, any
+    other call is recorded (a compute call must never be reached)."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        def fn(*args):
+            if name.endswith("_workspace_bytes"):
+                return 64
+            self.calls.append(name)
+            return 0
+        return fn
+
+
+@pytest.fixture
+def cpu_binding(monkeypatch):
+    """The binding with its GPU-residency check relaxed to CPU tensors and a
+    fake library, so that the shape checks run without a GPU."""
+    import torch
+
+    import bitwise_aligned_causal_amd as kb
+
+    def check_tensor(name, x, ndim=4):
+        if x.dtype != torch.bfloat16 or x.dim() != ndim or not x.is_contiguous():
+            raise ValueError(f"{name}: bad tensor")
+
+    fake = _FakeLib()
+    monkeypatch.setattr(kb, "_check_tensor", check_tensor)
+    monkeypatch.setattr(kb, "lib", lambda: fake)
+    return kb, fake
+
+
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_wrong_output_shape_before_any_launch(cpu_binding):
+    kb, fake = cpu_binding
+    q, k, v = _bf(1, 4, 64, 128), _bf(1, 1, 64, 128), _bf(1, 1, 64, 128)
+    q1 = _bf(1, 4, 1, 128)
+    small, wrong_heads = _bf(1, 4, 32, 128), _bf(1, 8, 64, 128)
+    calls = [
+        lambda: kb.prefill(q, k, v, out=small),
+        lambda: kb.prefill(q, k, v, out=wrong_heads),
+        lambda: kb.prefill_lse(q, k, v, out=small),
+        lambda: kb.partitioned(q, k, v, kv_len=64, out=small),
+        lambda: kb.partitioned_lse(q, k, v, kv_len=64, out=small),
+        lambda: kb.decode(q1, k, v, kv_len=64, out=_bf(1, 4, 2, 128)),
+        lambda: kb.decode_lse(q1, k, v, kv_len=64, out=_bf(2, 4, 1, 128)),
+        lambda: kb.decode_multi(_bf(1, 4, 2, 128), k, v, kv_len=64, out=_bf(1, 4, 1, 128)),
+        lambda: kb.prefill_varlen(_bf(4, 64, 128), _bf(1, 64, 128), _bf(1, 64, 128), [0, 64],
+                                  out=_bf(4, 63, 128)),
+        lambda: kb.prefill_varlen_lse(_bf(4, 64, 128), _bf(1, 64, 128), _bf(1, 64, 128), [0, 64],
+                                      out=_bf(4, 63, 128)),
+        lambda: kb.partitioned_varlen(_bf(4, 8, 128), _bf(1, 64, 128), _bf(1, 64, 128), [0, 8], [0, 64], [64],
+                                      out=_bf(4, 7, 128)),
+        lambda: kb.decode_varlen(_bf(4, 1, 128), _bf(1, 64, 128), _bf(1, 64, 128), [0, 64], [64],
+                                 out=_bf(2, 1, 128)),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError):
+            call()
+        assert fake.calls == [], f"case {i} reached the library"
+
+
+def test_binding_rejects_wrong_gradient_shapes_before_any_launch(cpu_binding, monkeypatch):
+    import torch
+
+    kb, fake = cpu_binding
+    q, k, v = _bf(1, 4, 64, 128), _bf(1, 1, 64, 128), _bf(1, 1, 64, 128)
+    o, do = _bf(1, 4, 64, 128), _bf(1, 4, 64, 128)
+    lse = torch.zeros((1, 4, 64), dtype=torch.float32)
+    # lse is an input that must live on the GPU; its own check is covered elsewhere
+    monkeypatch.setattr(kb, "_check_lse_in", lambda *a: None)
+    bad_grads = {"dq": _bf(1, 4, 32, 128), "dk": _bf(1, 2, 64, 128), "dv": _bf(1, 1, 63, 128)}
+    for name, bad in bad_grads.items():
+        with pytest.raises(ValueError, match=name):
+            kb.backward(q, k, v, o, do, lse, **{name: bad})
+        assert fake.calls == []
+    packed = {"dq": _bf(4, 63, 128), "dk": _bf(1, 64, 127), "dv": _bf(2, 64, 128)}
+    qp, kp, vp = _bf(4, 64, 128), _bf(1, 64, 128), _bf(1, 64, 128)
+    for name, bad in packed.items():
+        with pytest.raises(ValueError):
+            kb.backward_varlen(qp, kp, vp, _bf(4, 64, 128), _bf(4, 64, 128), torch.zeros((4, 64)), [0, 64],
+                               **{name: bad})
+        assert fake.calls == []
+
+
+def test_binding_accepts_matching_output(cpu_binding, monkeypatch):
+    kb, fake = cpu_binding
+    monkeypatch.setattr(kb, "_stream", lambda x: None)
+    q, k, v = _bf(1, 4, 64, 128), _bf(1, 1, 64, 128), _bf(1, 1, 64, 128)
+    out = _bf(1, 4, 64, 128)
+    assert kb.prefill(q, k, v, out=out) is out
+    assert fake.calls == ["kb_attn_prefill"]

@@ -132,12 +132,59 @@ def test_backward_row_forms_agree():
     np.testing.assert_array_equal(tail["dq"][:, :, 50:], full["dq"][:, :, 50:])
 
 
+def budgets_torch(q, k, v, do, scale):
+    """The error budgets from their definitions, in float64 matrix form
+    (torch, independent of the oracle's loops): with P the causal softmax,
+    dS = P (dO V^T - D), D_i = <dO_i, (P V)_i>, A_i = sum_j P_ij <|dO_i|, |v_j|>,
+      eq = scale (|dS| + P A) |K|,   ek = scale (|dS| + P A)^T |Q|,
+      ev = P^T |dO|,
+    with ek and ev summed over the query heads of each KV head."""
+    B, Hq, S, D = q.shape
+    g = Hq // k.shape[1]
+    Q, K, V, dO = (torch.from_numpy(f32(x)).double() for x in (q, k, v, do))
+    K, V = K.repeat_interleave(g, dim=1), V.repeat_interleave(g, dim=1)
+    scores = scale * Q @ K.transpose(-1, -2)
+    mask = torch.ones(S, S, dtype=torch.bool).triu(1)
+    P = torch.softmax(scores.masked_fill(mask, float("-inf")), dim=-1)
+    O = P @ V
+    Drow = (dO * O).sum(-1, keepdim=True)
+    dS = P * (dO @ V.transpose(-1, -2) - Drow)
+    A = (P * (dO.abs() @ V.abs().transpose(-1, -2))).sum(-1, keepdim=True)
+    W = dS.abs() + P * A
+    eq = scale * W @ K.abs()
+    ek = (scale * W.transpose(-1, -2) @ Q.abs()).reshape(B, Hq // g, g, S, D).sum(2)
+    ev = (P.transpose(-1, -2) @ dO.abs()).reshape(B, Hq // g, g, S, D).sum(2)
+    return eq.numpy(), ek.numpy(), ev.numpy()
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 45, 32), (2, 4, 1, 9, 8), (1, 4, 4, 3, 4)])
+def test_backward_budgets_equal_their_definition(shape):
+    # pinned from both sides: a budget inflated by a dropped weight or an extra
+    # factor, or one missing a term, differs from the matrix form
+    B, Hq, Hkv, S, D = shape
+    q, k, v, do = grads_inputs(37 + S, B, Hq, Hkv, S, D)
+    scale = 1.0 / math.sqrt(D)
+    g = oracle.backward(q, k, v, do, scale=scale, budgets=True)
+    for name, ref in zip(("eq", "ek", "ev"), budgets_torch(q, k, v, do, scale)):
+        np.testing.assert_allclose(g[name], ref, rtol=1e-11, atol=1e-13, err_msg=name)
+
+
 def test_backward_budgets_cover_terms():
     # the budgets are sums of the absolute values of the terms whose sums are
     # the gradients, so they bound the gradients themselves
     q, k, v, do = grads_inputs(37, 1, 8, 2, 45, 32)
     g = oracle.backward(q, k, v, do, budgets=True)
-    assert np.all(g["ev"] >= np.abs(g["dv"]) * (1 - 1e-12))
+    for grad, bud in (("dq", "eq"), ("dk", "ek"), ("dv", "ev")):
+        assert np.all(g[bud] >= np.abs(g[grad]) * (1 - 1e-12)), grad
+
+
+def test_value_budget_is_tight_for_nonnegative_upstream():
+    # with dO >= 0 every term P_ij dO_id of dV is >= 0, so the sum of their
+    # absolute values is dV itself: the budget may not exceed it
+    q, k, v, do = grads_inputs(41, 2, 8, 2, 30, 16)
+    do = kb_gen.f32_to_bf16_bits(np.abs(f32(do)))
+    g = oracle.backward(q, k, v, do, budgets=True)
+    np.testing.assert_allclose(g["ev"], g["dv"], rtol=1e-12, atol=0)
     assert np.all(g["eq"] >= np.abs(g["dq"]) * (1 - 1e-12))
     assert np.all(g["ek"] >= np.abs(g["dk"]) * (1 - 1e-12))
 

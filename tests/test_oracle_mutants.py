@@ -109,6 +109,13 @@ BWD_MUTANTS = {
                    "for (int64_t d = 0; d < D; ++d) Di += widen(dorow[d]) * widen(vrows[d]);")],
     "dk_to_wrong_group": [("b = x / Hkv;\n            g = x % Hkv;\n            h_first = g * hpg;",
                            "b = x / Hkv;\n            g = x % Hkv;\n            h_first = ((g + 1) % Hkv) * hpg;")],
+    # mistakes in the error budgets that leave every gradient bit unchanged
+    "ev_drops_weight": [("if (evb) evb[j * D + d] += w[j] * fabs((double)dod);",
+                         "if (evb) evb[j * D + d] += fabs((double)dod);")],
+    "ek_times_length": [("if (ekb) ekb[j * D + d] += (double)p->scale * (fabs((double)ds[j]) + w[j] * Ai)",
+                         "if (ekb) ekb[j * D + d] += (double)S * p->scale * (fabs((double)ds[j]) + w[j] * Ai)")],
+    "eq_drops_pa_term": [("if (eqr) bud += (fabs((double)ds[j]) + w[j] * Ai)",
+                          "if (eqr) bud += (fabs((double)ds[j]))")],
 }
 
 
@@ -127,6 +134,9 @@ def bwd_battery(entry) -> bool:
             ok &= bool(np.allclose(got[name], r, rtol=0, atol=1e-11 * max(1.0, np.abs(r).max())))
         lref = bp.masked_lse_torch(q, k, S, scale)
         ok &= bool(np.allclose(oracle.lse(q, k, v, scale=scale, entry=entry), lref, rtol=0, atol=1e-12))
+        bud = oracle.backward(q, k, v, do, scale=scale, budgets=True, entry=entry)
+        for name, r in zip(("eq", "ek", "ev"), bp.budgets_torch(q, k, v, do, scale)):
+            ok &= bool(np.allclose(bud[name], r, rtol=1e-11, atol=1e-13))
     return ok
 
 
