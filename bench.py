@@ -53,6 +53,20 @@ def prefill_flops(batch: int, n_rows_first_pos: int, n_rows: int) -> int:
     return 4 * D * s * batch * HQ
 
 
+def row_flops(positions) -> int:
+    """Algorithmic FLOPs of query rows at the given positions: QK^T and PV,
+    2*D each per visible key, 4*D*(pos+1) per row."""
+    positions = np.asarray(positions, dtype=np.int64)
+    return int((4 * D * (positions + 1)).sum())
+
+
+def backward_flops(batch: int, n_q_heads: int, seq_len: int, head_dim: int = D) -> int:
+    """Algorithmic FLOPs of the causal backward: five products of 2*D FLOPs
+    per visible (query, key) pair (S recomputed, dP, dV, dQ, dK)."""
+    pairs = seq_len * (seq_len + 1) // 2
+    return int(10 * head_dim * pairs * batch * n_q_heads)
+
+
 def source_hash(names) -> str:
     """Hash of kernel sources with comments and whitespace removed, and of the
     compiler flags they are built with, so that a counter summary stays valid
@@ -80,6 +94,52 @@ def device_env(torch, dev) -> dict:
     if clock:
         env["clock_mhz"] = round(clock / 1000)
     return env
+
+
+def gpu_clocks() -> dict | None:
+    """Clock levels as rocm-smi reports them (text fields, as printed), or None."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=60)
+        data = json.loads(r.stdout[r.stdout.index("{"):])
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
+    return {k.strip(" :"): v for k, v in card.items() if "clk" in k.lower() or "clock" in k.lower()} or None
+
+
+def git_head() -> dict:
+    """The commit the tree comes from: git itself in a checkout, else the record
+    the library build leaves beside libkb_attn.so (a copied tree has no .git)."""
+    import subprocess
+
+    try:
+        head = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                              timeout=30)
+        if head.returncode == 0:
+            dirty = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                                   capture_output=True, text=True, timeout=30)
+            return {"commit": head.stdout.strip(), "dirty": bool(dirty.stdout.strip()), "from": "git"}
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open(os.path.join(ROOT, "bitwise_aligned_causal_amd", "_build_info.json")) as fh:
+            rec = json.load(fh)
+        return {"commit": rec.get("git_head"), "dirty": rec.get("dirty"), "from": "build record"}
+    except (OSError, ValueError):
+        return {"commit": None, "dirty": None, "from": "unavailable"}
+
+
+def worst_error(got, ref, shape) -> dict:
+    """max-abs and mean-abs of got - ref and where the max sits: (b, h, row,
+    d) for a full [B, H, rows, D] output, or (flat row, d) for listed rows."""
+    err = np.abs(got - ref)
+    i = int(np.argmax(err))
+    idx = [int(x) for x in np.unravel_index(i, err.shape)]
+    where = dict(zip(shape, idx))
+    return {"max_abs": float(err.flat[i]), "mean_abs": float(err.mean()), "at": where,
+            "got": float(got.flat[i]), "ref": float(ref.flat[i])}
 
 
 def kernel_source_hash() -> str:
@@ -127,7 +187,7 @@ def cpu_baseline(q, k, v, target_s: float):
         t0 = time.perf_counter()
         refs.append(oracle.attention(q, k, v, rows=rows, threads=threads))
         dt += time.perf_counter() - t0
-        flops += oracle.row_flops(pos)
+        flops += row_flops(pos)
         all_rows.append(rows)
         rate = flops / max(dt, 1e-6)
         left = target_s - dt
@@ -136,7 +196,121 @@ def cpu_baseline(q, k, v, target_s: float):
     ref = np.concatenate(refs)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows.size} random prefill rows of the same B=16 S=16384 input (fp64 oracle), "
-                      f"{flops:.3e} FLOPs in {dt:.2f} s"}, rows, ref
+                      f"{flops:.3e} FLOPs in {dt:.2f} s",
+            "rows": int(rows.size), "seconds": round(dt, 3), "rows_per_s": round(rows.size / dt, 1)}, rows, ref
+
+
+def prefill_workloads(kb, torch, dev, stream, reps: int = 5):
+    """The pages' prefill set (B=1, S = 1K, 4K, 8K and 16K, N(0,1), seed 17;
+    S=1024 is the worked example's case) and the two other prefill workloads
+    (B=4 S=4096, seed 2; B=8 S=8192, seed 3, also as its 8 partitioned calls
+    of 1024 rows against the cache), each timed alone with HIP events on the
+    launch stream (median of `reps` after one untimed call).  Returns the
+    rows for the JSON line and the host copies the CPU leg checks."""
+    import kb_gen
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    def to_dev(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    rows, keep = [], {}
+    cases = [("pages B=1", 17, 1, 1024), ("pages B=1", 17, 1, 4096), ("pages B=1", 17, 1, 8192),
+             ("pages B=1", 17, 1, 16384), ("B=4 S=4096", 2, 4, 4096), ("B=8 S=8192", 3, 8, 8192)]
+    for name, seed, bs, sl in cases:
+        q, k, v = kb_gen.attention_inputs(seed, bs, sl)
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        out = torch.empty_like(qd)
+        ms = timed(lambda: kb.prefill(qd, kd, vd, out=out))
+        fl = 2 * bs * HQ * D * sl * (sl + 1)
+        rec = {"workload": name, "batch": bs, "seq_len": sl, "seed": seed, "ms": round(ms, 4),
+               "tflops": round(fl / ms / 1e9, 2), "frac_of_peak": round(fl / (ms * 1e-3) / PEAK_BF16, 4),
+               "workgroups": bs * HKV * ((sl + 63) // 64)}
+        if bs == 8:
+            chunks = [qd[:, :, c * PART:(c + 1) * PART].contiguous() for c in range(sl // PART)]
+            outs = [torch.empty_like(c) for c in chunks]
+
+            def parts():
+                for c in range(sl // PART):
+                    kb.partitioned(chunks[c], kd, vd, kv_len=(c + 1) * PART, out=outs[c])
+            pms = timed(parts)
+            mism = sum(int((outs[c].view(torch.int16) != out.view(torch.int16)[:, :, c * PART:(c + 1) * PART])
+                           .sum()) for c in range(sl // PART))
+            rec["partitioned"] = {"calls": sl // PART, "rows_per_call": PART, "ms": round(pms, 4),
+                                  "tflops": round(fl / pms / 1e9, 2),
+                                  "frac_of_peak": round(fl / (pms * 1e-3) / PEAK_BF16, 4),
+                                  "bitwise_mismatch_vs_prefill": mism}
+            del chunks, outs
+        if (bs, sl) in ((1, 1024), (4, 4096)):
+            keep[(bs, sl)] = (q, k, v, out.view(torch.int16).cpu().numpy())
+        rows.append(rec)
+        del qd, kd, vd, out
+    return rows, keep
+
+
+def cpu_leg(q, k, v, out_pre, keep, sweep_cells, target_s: float, dev, torch):
+    """The oracle as it stands, on the host cores of this run: (1) the worked
+    example's case B=1 S=1024 in full on all threads and on one thread, (2)
+    B=4 S=4096 in full, (3) every decode-sweep cell, (4) randomly sampled rows
+    of the bench's B=16 S=16384 input for about target_s seconds.  Each is also
+    the parity check of the GPU output it covers."""
+    import kb_gen
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    full = {}
+    for (bs, sl), (qq, kk, vv, bits) in sorted(keep.items()):
+        t0 = time.perf_counter()
+        ref = oracle.attention(qq, kk, vv, threads=threads)
+        dt = time.perf_counter() - t0
+        got = kb_gen.bf16_bits_to_f32(bits.view(np.uint16)).astype(np.float64)
+        nrows = bs * HQ * sl
+        rec = {"seconds": round(dt, 3), "threads": threads, "rows": nrows, "rows_per_s": round(nrows / dt, 1),
+               "tflops": round(2 * bs * HQ * D * sl * (sl + 1) / dt / 1e12, 5),
+               "check": worst_error(got, ref, ("b", "h", "row", "d"))}
+        if (bs, sl) == (1, 1024):
+            t0 = time.perf_counter()
+            oracle.attention(qq, kk, vv, threads=1)
+            rec["single_thread_seconds"] = round(time.perf_counter() - t0, 3)
+        full[f"B={bs} S={sl}"] = rec
+    # decode sweep cells: one query row per head at position kv_len - 1
+    t_dec, n_dec, worst = 0.0, 0, None
+    for bs, ctx, got_bits in sweep_cells:
+        qs = np.ascontiguousarray(q[:bs, :, ctx - 1:ctx])
+        t0 = time.perf_counter()
+        ref = oracle.attention(qs, np.ascontiguousarray(k[:bs]), np.ascontiguousarray(v[:bs]), kv_len=ctx,
+                               threads=threads)
+        t_dec += time.perf_counter() - t0
+        n_dec += bs * HQ
+        w = worst_error(kb_gen.bf16_bits_to_f32(got_bits.view(np.uint16)).astype(np.float64), ref,
+                        ("b", "h", "row", "d"))
+        w["cell"] = {"batch": bs, "kv_len": ctx}
+        if worst is None or w["max_abs"] > worst["max_abs"]:
+            worst = w
+    full["decode sweep (16 cells)"] = {"seconds": round(t_dec, 3), "threads": threads, "rows": n_dec,
+                                       "rows_per_s": round(n_dec / max(t_dec, 1e-9), 1), "check": worst}
+    base, rows, ref = cpu_baseline(q, k, v, target_s)
+    flat = out_pre.view(-1, D)
+    got = flat[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+    check = worst_error(got, ref, ("flat_row", "d"))
+    fr = check["at"]["flat_row"]
+    check["at"] = {"b": int(rows[fr] // (HQ * S)), "h": int(rows[fr] // S % HQ), "row": int(rows[fr] % S),
+                   "d": check["at"]["d"]}
+    check.update({"rows": int(rows.size), "tol_max_abs": 2e-2, "tol_mean_abs": 2e-3})
+    base["full_oracle"] = full
+    return base, check
 
 
 def backward_section(kb, torch, dev, qd, kd, vd, out_pre, reps: int, check: bool):
@@ -148,7 +322,6 @@ def backward_section(kb, torch, dev, qd, kd, vd, out_pre, reps: int, check: bool
     output must equal the plain prefill's bit for bit, and a second backward
     must reproduce the gradients bit for bit."""
     import kb_gen
-    import oracle
 
     stream = torch.cuda.current_stream(dev)
     do = torch.from_numpy(kb_gen.normal_bf16(SEED, 4, (B, HQ, S, D)).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -166,7 +339,7 @@ def backward_section(kb, torch, dev, qd, kd, vd, out_pre, reps: int, check: bool
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     ms = float(np.median(times))
-    flops = oracle.backward_flops(B, HQ, S, D)
+    flops = backward_flops(B, HQ, S, D)
     res = {"batch": B, "seq_len": S, "ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 2),
            "frac_of_peak": round(flops / (ms * 1e-3) / PEAK_BF16, 4), "flops": flops,
            "flops_count": "5 products x 2*D per visible (query, key) pair"}
@@ -187,7 +360,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the decode sweep and the ragged batch (profiling runs: one kernel configuration each)")
@@ -292,11 +465,12 @@ def main() -> int:
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
 
-    sweep, varlen, paged, decode_multi = None, None, None, None
+    sweep, varlen, paged, decode_multi, pre_sweep = None, None, None, None, None
+    sweep_cells, keep = [], {}
     if not args.no_extras:
         # decode sweep: batch 1/4/8/16 x context 128/1K/4K/8K over the resident
         # cache (capacity 16384, first kv_len keys), cold, one query token per head
-        sweep = []
+        sweep, sweep_cells = [], []
         for bs in (1, 4, 8, 16):
             for ctx in (128, 1024, 4096, 8192):
                 qs = qd[:bs, :, ctx - 1:ctx].contiguous()
@@ -315,6 +489,7 @@ def main() -> int:
                 nbytes = 4096 * bs * ctx + 16384 * bs
                 sweep.append({"batch": bs, "kv_len": ctx, "us_cold": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
                               "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / PEAK_HBM, 4)})
+                sweep_cells.append((bs, ctx, os_.view(torch.int16).cpu().numpy()))
 
         # ragged batch: 16 sequences of mixed lengths, sequence i = the first L_i
         # rows of batch i, packed head-major; its rows must equal the dense
@@ -420,6 +595,16 @@ def main() -> int:
         del qm, om, wsm
     del flush
     backward = None if args.no_extras else backward_section(kb, torch, dev, qd, kd, vd, out_pre, reps=3, check=True)
+    if not args.no_extras:
+        pre_sweep, keep = prefill_workloads(kb, torch, dev, stream)
+    # clock levels while the GPU is busy with prefill launches (about 1.2 s
+    # of queued work), then idle
+    clocks_busy = None
+    if not args.no_extras:
+        for _ in range(40):
+            kb.prefill(qd, kd, vd, out=out_pre)
+        clocks_busy = gpu_clocks()
+        torch.cuda.synchronize()
 
     pre_ms = float(np.mean(times["pre"]))
     part_ms = float(np.mean(times["part"]))
@@ -447,7 +632,9 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
                      "traffic": traffic, "kernel": "prefill_kernel<false>", "launch_ms": round(pre_ms, 3),
-                     "flops_per_launch": f_pre},
+                     "flops_per_launch": f_pre,
+                     "timing": "HIP events on the launch stream around each of the timed steps' prefill launches, "
+                               "mean"},
         "prefill": {"ms": round(pre_ms, 3), "tflops": round(f_pre / pre_ms / 1e9, 2),
                     "frac_of_peak": round(f_pre / (pre_ms * 1e-3) / PEAK_BF16, 4)},
         "partitioned": {"calls": S // PART, "ms": round(part_ms, 3), "tflops": round(f_part / part_ms / 1e9, 2),
@@ -457,6 +644,7 @@ def main() -> int:
                    "ms_cold": round(cold_ms, 4), "gbs_cold": round(dec_bytes / cold_ms / 1e6, 1),
                    "frac_of_peak_cold": round(dec_bytes / (cold_ms * 1e-3) / PEAK_HBM, 4)},
         "decode_sweep": sweep,
+        "prefill_sweep": pre_sweep,
         "varlen": varlen,
         "paged_decode": paged,
         "decode_multi": decode_multi,
@@ -466,16 +654,13 @@ def main() -> int:
         "kernel_source_hash": kernel_source_hash(),
         "inputs_sha256": {name: hashlib.sha256(np.ascontiguousarray(x).data).hexdigest()[:16]
                           for name, x in (("q", q), ("k", k), ("v", v))},
-        "env": device_env(torch, dev),
+        "env": {**device_env(torch, dev), "clocks_idle": gpu_clocks(), "clocks_busy": clocks_busy},
+        "git": git_head(),
     }
     if not args.no_cpu_baseline:
-        base, rows, ref = cpu_baseline(q, k, v, args.cpu_seconds)
-        flat = out_pre.view(-1, D)
-        got = flat[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
-        err = np.abs(got - ref)
+        base, check = cpu_leg(q, k, v, out_pre, keep, sweep_cells, args.cpu_seconds, dev, torch)
         result["cpu_baseline"] = base
-        result["oracle_check"] = {"rows": int(rows.size), "max_abs": float(err.max()),
-                                  "mean_abs": float(err.mean()), "tol_max_abs": 2e-2, "tol_mean_abs": 2e-3}
+        result["oracle_check"] = check
     print(json.dumps(result))
     return 0
 

@@ -1,13 +1,14 @@
 """Turn rocprofv3 output of bench.py into the short summaries kept in profiles/.
 
 The GPU runs (each command runs committed files only):
-  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras
+  rocprofv3 --kernel-trace --stats -d <stats> -o run --output-format csv -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extras
   rocprofv3 --pmc FETCH_SIZE -d <fetch> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras
   rocprofv3 --pmc WRITE_SIZE -d <write> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras
   rocprofv3 --pmc FETCH_SIZE -d <copy_fetch> -o run --output-format csv -- python3 bench.py --copy-probe
   rocprofv3 --pmc WRITE_SIZE -d <copy_write> -o run --output-format csv -- python3 bench.py --copy-probe
   rocprofv3 --pmc <8 SQ counters> -d <sqN> -o run --output-format csv -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras
-      (two passes, SQ_PASSES below)
+      (three passes, SQ_PASSES below; the third reads the GPU's active cycles, so that
+      cycles / dispatch time gives the clock the kernel ran at)
   and for the backward kernels, the same --kernel-trace --stats, FETCH_SIZE and
   WRITE_SIZE runs of `python3 bench.py --backward-only 3`.
 Then, on any host:
@@ -35,7 +36,10 @@ SQ_PASSES = (
     "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS",
     "SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU "
     "SQ_LDS_ADDR_CONFLICT SQ_INSTS_VALU_MFMA_MOPS_BF16",
+    "GRBM_GUI_ACTIVE GRBM_COUNT",
 )
+STATS_ARGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-extras"
+STATS_WARMUP_STEPS = 2
 KERNELS = {
     "prefill_kernel<false>": ("prefill_kernel_b16_s16384", "full causal prefill B=16 S=16384 (one launch per step)"),
     "prefill_kernel<true>": ("prefill_kernel_partitioned_b16_16x1024",
@@ -86,6 +90,27 @@ def per_dispatch(d: str):
     return out
 
 
+def trace_durations(d: str, kernels) -> dict:
+    """{kernel: [duration ns in dispatch order]} from a --kernel-trace run."""
+    rows = []
+    for r in csv.DictReader(open(find_csv(d, "kernel_trace.csv"))):
+        k = short(r["Kernel_Name"], kernels)
+        if k:
+            rows.append((int(r["Dispatch_Id"]), k, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for _, k, dur in sorted(rows):
+        out.setdefault(k, []).append(dur)
+    return out
+
+
+def steady_average(durs, warmup_steps: int, steps: int):
+    """Mean duration over the timed steps' dispatches: the first warmup_steps
+    steps' dispatches (untimed warm-up, first touches of the inputs) dropped."""
+    per_step = max(1, len(durs) // (warmup_steps + steps))
+    kept = durs[warmup_steps * per_step:] or durs
+    return statistics.mean(kept), len(kept)
+
+
 def copy_factor(d: str) -> float:
     vals = [v for name, rows in per_dispatch(d).items() if "copyBuffer" in name for (_, _, v, _) in rows]
     return COPY_BYTES / 1024.0 / statistics.mean(vals)
@@ -105,7 +130,7 @@ def sq_summary(dirs, out: str, src_hash: str) -> None:
         for name, rows in per_counter(d).items():
             vals.update(rows)
     tiles = prefill_wave_tiles()
-    lines = [f"# prefill_kernel<false> SQ counters, B={bench.B} S={bench.S} ({tiles / 8:.3g} workgroup-tiles x 8 waves)",
+    lines = [f"# prefill_kernel<false> SQ and GRBM counters, B={bench.B} S={bench.S} ({tiles / 8:.3g} workgroup-tiles x 8 waves)",
              f"kernel hash (code without comments, and compiler flags): {src_hash}", "",
              "commands (one pass each, counters split to stay within the SQ block limit):"]
     lines += [f"  rocprofv3 --pmc {p} -d <dir> -o run --output-format csv -- "
@@ -117,6 +142,15 @@ def sq_summary(dirs, out: str, src_hash: str) -> None:
         util = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * vals["SQ_BUSY_CU_CYCLES"])
         lines += ["", f"MFMA utilisation: SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES) = {util:.3f} of the "
                       "SIMD cycles while the CUs are busy (at the clock the chip runs under this load)"]
+    if "GRBM_COUNT" in vals and "GRBM_GUI_ACTIVE" in vals:
+        dur = [d for name, rows in per_dispatch(dirs[-1]).items() if short(name) == "prefill_kernel<false>"
+               for (_, _, _, d) in rows]
+        if dur:
+            sec = statistics.mean(dur) * 1e-9
+            # the GRBM counters are summed over the 8 XCDs (each counts its own clock)
+            lines += ["", f"clock under this load: GRBM_COUNT / (8 XCDs x dispatch time {sec * 1e3:.2f} ms) = "
+                          f"{vals['GRBM_COUNT'] / (8 * sec) / 1e6:.0f} MHz; GRBM_GUI_ACTIVE / GRBM_COUNT = "
+                          f"{vals['GRBM_GUI_ACTIVE'] / vals['GRBM_COUNT']:.3f}"]
     with open(os.path.join(out, "prefill_kernel_b16_s16384_sq_counters.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -130,7 +164,8 @@ def per_counter(d: str):
     return out
 
 
-def write_summaries(kernels, stats, fetch, write, f_fetch, f_write, src_hash, out, stats_args, pmc_args, flops):
+def write_summaries(kernels, stats, fetch, write, f_fetch, f_write, src_hash, out, stats_args, pmc_args, flops,
+                    trace=None, warmup_steps=0, steps=0):
     for k, (fname, what) in kernels.items():
         st = stats.get(k)
         fr = [v for n, rows in fetch.items() if short(n, kernels) == k for v in rows]
@@ -140,7 +175,11 @@ def write_summaries(kernels, stats, fetch, write, f_fetch, f_write, src_hash, ou
         fetch_kib = statistics.mean(v for _, _, v, _ in fr)
         write_kib = statistics.mean(v for _, _, v, _ in wr)
         hbm = (fetch_kib * f_fetch + write_kib * f_write) * 1024.0
-        avg_us = float(st["AverageNs"]) / 1e3
+        avg_all_us = float(st["AverageNs"]) / 1e3
+        avg_us, n_kept = avg_all_us, int(st["Calls"])
+        if trace and trace.get(k) and warmup_steps:
+            avg_ns, n_kept = steady_average(trace[k], warmup_steps, steps)
+            avg_us = avg_ns / 1e3
         lines = [
             f"# {k}: {what}",
             f"kernel hash (code without comments, and compiler flags): {src_hash}",
@@ -155,9 +194,11 @@ def write_summaries(kernels, stats, fetch, write, f_fetch, f_write, src_hash, ou
             "[--bwd-stats <s> --bwd-fetch <f> --bwd-write <w>] --out profiles",
             "",
             "kernel-trace --stats:",
-            f"  calls {st['Calls']}, average {avg_us:.1f} us, "
+            f"  calls {st['Calls']}, average {avg_all_us:.1f} us, "
             f"min {float(st['MinNs']) / 1e3:.1f} us, max {float(st['MaxNs']) / 1e3:.1f} us, "
             f"{float(st['Percentage']):.2f} % of GPU time",
+            f"  average over the {n_kept} dispatches of the timed steps (warm-up steps' dispatches dropped): "
+            f"{avg_us:.1f} us",
             "",
             "counters (per dispatch, mean over the profiled dispatches):",
             f"  dispatches {len(fr)}, FETCH_SIZE {fetch_kib:.1f} KiB, WRITE_SIZE {write_kib:.1f} KiB",
@@ -166,7 +207,8 @@ def write_summaries(kernels, stats, fetch, write, f_fetch, f_write, src_hash, ou
             f"  HBM bytes per dispatch (scaled): {hbm:.4e}",
         ]
         if k in flops:
-            lines += ["", f"executed MFMA FLOPs per dispatch: {flops[k]:.4e} -> "
+            lines += ["", f"FLOPs per dispatch (algorithmic for the forward kernels, mean over the calls; "
+                          f"products executed for the backward ones): {flops[k]:.4e} -> "
                           f"{flops[k] / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s at the average duration "
                           f"({flops[k] / (avg_us * 1e-6) / bench.PEAK_BF16:.3f} of the 2.5 PFLOP/s bf16 peak)"]
         with open(os.path.join(out, fname + ".txt"), "w") as fh:
@@ -197,8 +239,10 @@ def main():
     src_hash = bench.kernel_source_hash()
     os.makedirs(args.out, exist_ok=True)
     write_summaries(KERNELS, stats, per_dispatch(args.fetch), per_dispatch(args.write), f_fetch, f_write, src_hash,
-                    args.out, "--steps 3 --warmup 1 --no-cpu-baseline --no-extras",
-                    "--steps 1 --warmup 0 --no-cpu-baseline --no-extras", {})
+                    args.out, STATS_ARGS, "--steps 1 --warmup 0 --no-cpu-baseline --no-extras",
+                    {"prefill_kernel<false>": bench.prefill_flops(bench.B, 0, bench.S),
+                     "prefill_kernel<true>": bench.prefill_flops(bench.B, 0, bench.S) // (bench.S // bench.PART)},
+                    trace_durations(args.stats, KERNELS), STATS_WARMUP_STEPS, 5)
     if args.bwd_stats:
         bstats = {}
         for r in csv.DictReader(open(find_csv(args.bwd_stats, "kernel_stats.csv"))):

@@ -47,7 +47,29 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd))
     os.replace(tmp, LIB)
+    write_build_info()
     return LIB
+
+
+def write_build_info() -> None:
+    """Record beside the library the commit it was built from, for runs on a
+    copy of the tree that has no .git (the benchmark reports it)."""
+    import datetime
+    import json
+
+    def git(*args):
+        try:
+            r = subprocess.run(["git", "-C", ROOT, *args], capture_output=True, text=True, timeout=30)
+            return r.stdout.strip() if r.returncode == 0 else None
+        except (OSError, subprocess.SubprocessError):
+            return None
+
+    head = git("rev-parse", "HEAD")
+    dirty = git("status", "--porcelain", "--untracked-files=no")
+    rec = {"git_head": head, "dirty": None if dirty is None else bool(dirty),
+           "built_utc": datetime.datetime.now(datetime.timezone.utc).isoformat(timespec="seconds")}
+    with open(os.path.join(PKG, "_build_info.json"), "w") as fh:
+        json.dump(rec, fh)
 
 
 if __name__ == "__main__":

@@ -145,12 +145,6 @@ def weights(q, k, v, row: int, kv_len: int | None = None, scale: float | None = 
     return out
 
 
-def row_flops(positions) -> int:
-    """Algorithmic FLOPs of the rows at the given positions: 4*D*(pos+1) each with D=128."""
-    positions = np.asarray(positions, dtype=np.int64)
-    return int((4 * 128 * (positions + 1)).sum())
-
-
 def _check_bwd(q, k, v, dout):
     _check(q, k, v)
     if dout.dtype != np.uint16 or dout.shape != q.shape or not dout.flags.c_contiguous:
@@ -204,10 +198,3 @@ def backward_dq_rows(q, k, v, dout, rows, scale: float | None = None, budgets: b
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return dq, eq
-
-
-def backward_flops(batch: int, n_q_heads: int, seq_len: int, head_dim: int = 128) -> int:
-    """Algorithmic FLOPs of the causal backward: five products of 2*D FLOPs
-    per visible (query, key) pair (S recomputed, dP, dV, dQ, dK)."""
-    pairs = seq_len * (seq_len + 1) // 2
-    return int(10 * head_dim * pairs * batch * n_q_heads)
