@@ -344,9 +344,11 @@ __device__ __forceinline__ f32x16 zero16() {
 //   o[db]   : O^T accumulators for d rows 32*(dblk0+db) .. +31 of column j
 // ---------------------------------------------------------------------------
 // The reference max moves only when a tile's max exceeds it by more than
-// kLazyTau (log2 units), so P <= 2^64, a chunk's row sum <= 2^74 and its
-// accumulators <= 2^74 max|v|, inside the fp32 / bf16 range for |v| < 2^54;
-// relative rounding does not depend on the scale.  A high threshold makes the
+// kLazyTau (log2 units), so P <= 2^64 relative to the reference: a chunk's
+// row sum is at most 2^74 and its accumulators 2^74 max|v|, and after the
+// chunk fold a row's totals reach kv_len 2^64 and kv_len 2^64 max|v|, inside
+// the fp32 range while kv_len max|v| < 2^64; relative rounding does not
+// depend on the scale.  A high threshold makes the
 // O rescale rare: on queries and keys with strong outlier channels (score
 // spread of about 16 log2 units) a threshold of 8 rescales on about 2 tiles in
 // 3, 32 on about 1 in 6 (mostly the first tile of a chunk, which skips it).

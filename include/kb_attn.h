@@ -6,12 +6,13 @@
  * The operator is the unified attention of the KernelBraid / AReaL-TIK README:
  *   - "Features": BF16, causal, contiguous [batch, heads, sequence, head_dim]
  *     tensors, 32 query heads, 8 KV heads, head_dim 128;
- *   - "Usage": a causal full-sequence forward (unified_prefill) and a
- *     one-token decode over the same KV context (unified_decode) whose output
- *     equals the last prefill row bit for bit; the output has the shape of q;
- *   - "Method" / "Advantages": one numerical contract links full-sequence
- *     prefill, partitioned forward and one-token decode, so all three give
- *     bitwise-identical outputs for the same inputs and context.
+ *   - "Usage": two calls, unified_prefill (the whole causal sequence) and
+ *     unified_decode (the last token against all cached keys); the decoded
+ *     row and the prefill's last row are compared as raw bf16 bits, and each
+ *     result takes q's shape;
+ *   - "Method" / "Advantages": prefill, the chunked (partitioned) forward and
+ *     one-token decode follow one set of numerical rules, which is what makes
+ *     their results for a given row and context the same bit pattern.
  *
  * Numerical contract (shared by every entry point): for the query row at
  * absolute position pos (keys 0..pos visible, KV head = q head / 4),
@@ -34,7 +35,11 @@
  *   - q, k and v must hold finite values.  Scores are accumulated in fp32, so
  *     a row whose scale * <q, k_j> leaves the fp32 range (about 3.4e38) is
  *     outside the contract and its output is not specified; the library does
- *     not check the values (that would cost a pass over the cache).
+ *     not check the values (that would cost a pass over the cache).  The
+ *     softmax weights are kept relative to a reference maximum that may lag
+ *     the true one by up to 2^64, so a row's running sums reach at most
+ *     kv_len * 2^64 and kv_len * 2^64 * max|v|; the contract also needs
+ *     kv_len * max|v| < 2^64 (|v| < 2^34 at the longest kv_len, 2^30).
  *   - The caller owns every buffer; the library allocates nothing, keeps no
  *     state and is thread-safe.  Calls are asynchronous on `stream` (0 = the
  *     null stream) and return once the work is enqueued.
