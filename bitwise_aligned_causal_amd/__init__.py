@@ -10,6 +10,7 @@ Entry points (KernelBraid / AReaL-TIK README, "Usage" and "Method"):
   prefill(q, k, v)                          causal full-sequence forward
   partitioned(q, k_cache, v_cache, kv_len)  a chunk of rows against cached KV
   decode(q, k_cache, v_cache, kv_len)       one query token
+  decode_static(q, k_cache, v_cache, kv_len) the same without a workspace (library-held scratch)
   decode_multi(q, k_cache, v_cache, kv_len) the last 1..8 tokens (a short partitioned chunk, split-KV)
   unified_prefill / unified_decode          the README's call shapes
   prefill_varlen / partitioned_varlen / decode_varlen
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.kb_attn_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32, vp, ctypes.c_size_t,
                                      vp]
         L.kb_attn_decode.restype = ctypes.c_int
+        L.kb_attn_decode_static.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, f32, vp]
+        L.kb_attn_decode_static.restype = ctypes.c_int
         L.kb_attn_decode_workspace_bytes.argtypes = [i64, i64, i32, i32]
         L.kb_attn_decode_workspace_bytes.restype = ctypes.c_size_t
         p64 = ctypes.POINTER(i64)
@@ -232,6 +235,30 @@ def decode(q, k_cache, v_cache, kv_len: int | None = None, scale: float | None =
                                k_cache.shape[2], Hq, k_cache.shape[1], D, _scale(scale, D), ws_ptr, ws_bytes,
                                _stream(q)))
     return out
+
+
+def decode_static(q, k_cache, v_cache, kv_len: int | None = None, scale: float | None = None, out=None):
+    """decode() without a workspace: the chunk partials go to the library's
+    own per-GPU scratch (8 MiB), so the call allocates nothing when out is
+    given.  Calls that may overlap on one GPU race on that scratch."""
+    for n, x in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(n, x)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache))
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per sequence")
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shape mismatch")
+    kv_len = k_cache.shape[2] if kv_len is None else int(kv_len)
+    out = _torch().empty_like(q) if out is None else out
+    _check_like("out", out, q)
+    check(lib().kb_attn_decode_static(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B,
+                                      kv_len, k_cache.shape[2], Hq, k_cache.shape[1], D, _scale(scale, D),
+                                      _stream(q)))
+    return out
+
+
+DECODE_STATIC_SCRATCH_BYTES = 8 << 20
 
 
 def decode_multi_workspace_bytes(batch: int, n_rows: int, kv_len: int, n_q_heads: int = 32,
@@ -571,7 +598,7 @@ def unified_decode(q_last, k, v, H_Q: int, H_KV: int, scale: float | None = None
     return decode(q_last, k, v, k.shape[2], scale)
 
 
-__all__ = ["prefill", "partitioned", "decode", "unified_prefill", "unified_decode", "contract",
+__all__ = ["prefill", "partitioned", "decode", "decode_static", "unified_prefill", "unified_decode", "contract",
            "decode_workspace_bytes", "prefill_varlen", "partitioned_varlen", "decode_varlen",
            "decode_varlen_workspace_bytes", "decode_paged", "prefill_lse", "partitioned_lse", "decode_lse",
            "decode_multi", "decode_multi_workspace_bytes", "backward", "backward_workspace_bytes", "prefill_varlen_lse", "backward_varlen",

@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 #include <vector>
@@ -660,6 +661,15 @@ __global__ __launch_bounds__(128) void combine_varlen_kernel(DecodeVarlenArgs a,
                 a.o + ((int64_t)t.seq[s] * a.tok_stride + (int64_t)head * a.head_stride) * kHeadDim, nullptr);
 }
 
+}  // namespace kb
+
+// Partials of kb_attn_decode_static (for callers that cannot allocate): one
+// copy per GPU, held until the process ends.  Host code never uses this name
+// as an address; it looks up each device's copy (static_scratch below).
+static __device__ __align__(256) float scratch[KB_ATTN_DECODE_STATIC_SCRATCH_BYTES / sizeof(float)];
+
+namespace kb {
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -710,6 +720,31 @@ int check_device(std::initializer_list<const void*> ptrs) {
 }
 
 int64_t n_chunks_of(int64_t kv_len) { return (kv_len + kChunk - 1) / kChunk; }
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (hipGetSymbolAddress with that device current) and kept.
+constexpr int kMaxDevices = 64;
+int static_scratch(void** out) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return KB_ATTN_ERR_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return KB_ATTN_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return KB_ATTN_ERR_HIP;
+        }
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return KB_ATTN_OK;
+}
 
 int launch_prefill(bool partitioned, const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t batch, int64_t q_len, int64_t kv_len, int64_t cap, int32_t n_kv_heads, float scale,
@@ -917,9 +952,12 @@ int partitioned_entry(const void* q, const void* k_cache, const void* v_cache, v
                           stream);
 }
 
+// With static_ws the partials go to the library's `scratch` array instead of
+// a caller workspace (workspace and workspace_bytes are ignored).
 int decode_entry(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int64_t batch,
                  int64_t n_rows, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
-                 int32_t head_dim, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                 int32_t head_dim, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                 bool static_ws = false) {
     if (!q || !k_cache || !v_cache || !o || batch < 1) return KB_ATTN_ERR_INVALID_ARG;
     if (int rc = check_heads(n_q_heads, n_kv_heads, head_dim)) return rc;
     if (int rc = check_scale(scale)) return rc;
@@ -927,7 +965,14 @@ int decode_entry(const void* q, const void* k_cache, const void* v_cache, void* 
     if (kv_len < n_rows || kv_len > kv_capacity) return KB_ATTN_ERR_LENGTH;
     if (kv_capacity > kMaxLen || batch * n_kv_heads > INT32_MAX) return KB_ATTN_ERR_LENGTH;
     const size_t need = kb_attn_decode_multi_workspace_bytes(batch, n_rows, kv_len, n_q_heads, head_dim);
-    if (need && (!workspace || workspace_bytes < need)) return KB_ATTN_ERR_WORKSPACE;
+    if (static_ws) {
+        // the scratch array is no caller buffer: nothing can alias it and it
+        // is device memory of every device by construction
+        if (need > KB_ATTN_DECODE_STATIC_SCRATCH_BYTES) return KB_ATTN_ERR_SCRATCH;
+        workspace = nullptr;
+        workspace_bytes = 0;
+    }
+    if (!static_ws && need && (!workspace || workspace_bytes < need)) return KB_ATTN_ERR_WORKSPACE;
     if (int rc = check_aligned({q, k_cache, v_cache, o, need ? workspace : nullptr})) return rc;
     const size_t qbytes = (size_t)batch * n_q_heads * n_rows * kHeadDim * 2;
     const size_t kvbytes = (size_t)batch * n_kv_heads * kv_capacity * kHeadDim * 2;
@@ -942,6 +987,8 @@ int decode_entry(const void* q, const void* k_cache, const void* v_cache, void* 
                             {need ? workspace : nullptr, need}}))
         return rc;
     if (int rc = check_device({q, k_cache, v_cache, o, need ? workspace : nullptr})) return rc;
+    if (static_ws && need)
+        if (int rc = static_scratch(&workspace)) return rc;
 
     const int64_t nc = n_chunks_of(kv_len);
     const int64_t rows = batch * n_q_heads * n_rows;
@@ -1023,6 +1070,13 @@ int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return decode_entry(q, k_cache, v_cache, o, nullptr, batch, 1, kv_len, kv_capacity, n_q_heads, n_kv_heads,
                         head_dim, scale, workspace, workspace_bytes, stream);
+}
+
+int kb_attn_decode_static(const void* q, const void* k_cache, const void* v_cache, void* o, int64_t batch,
+                          int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads, int32_t n_kv_heads,
+                          int32_t head_dim, float scale, hipStream_t stream) {
+    return decode_entry(q, k_cache, v_cache, o, nullptr, batch, 1, kv_len, kv_capacity, n_q_heads, n_kv_heads,
+                        head_dim, scale, nullptr, 0, stream, true);
 }
 
 int kb_attn_decode_lse(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int64_t batch,
@@ -1236,6 +1290,7 @@ const char* kb_attn_strerror(int code) {
         case KB_ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
         case KB_ATTN_ERR_ALIAS: return "output overlaps an input or the workspace";
         case KB_ATTN_ERR_HIP: return "HIP launch failed";
+        case KB_ATTN_ERR_SCRATCH: return "the call needs more than the library's 8 MiB static decode scratch";
         default: return "unknown error code";
     }
 }

@@ -72,7 +72,8 @@ enum {
     KB_ATTN_ERR_DEVICE = -5,      /* a pointer is not device memory of the current device */
     KB_ATTN_ERR_WORKSPACE = -6,   /* decode workspace missing or too small */
     KB_ATTN_ERR_ALIAS = -7,       /* the output overlaps an input or the workspace */
-    KB_ATTN_ERR_HIP = -8          /* a HIP call or kernel launch failed */
+    KB_ATTN_ERR_HIP = -8,         /* a HIP call or kernel launch failed */
+    KB_ATTN_ERR_SCRATCH = -9      /* the call needs more than the library's static scratch */
 };
 
 /*
@@ -116,6 +117,30 @@ int kb_attn_decode(const void* q, const void* k_cache, const void* v_cache, void
  * 0 for invalid sizes). */
 size_t kb_attn_decode_workspace_bytes(int64_t batch, int64_t kv_len, int32_t n_q_heads,
                                       int32_t head_dim);
+
+/* Size of the scratch array behind kb_attn_decode_static (8 MiB). */
+#define KB_ATTN_DECODE_STATIC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * kb_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The chunk partials go to a scratch array
+ * the library keeps in device memory, one copy per GPU it runs on, held until
+ * the process ends; the first call on a device looks up that device's copy.
+ * The call allocates nothing.  A call that needs more than
+ * KB_ATTN_DECODE_STATIC_SCRATCH_BYTES (kb_attn_decode_workspace_bytes(...) of
+ * the same sizes; B * n_q_heads * ceil(kv_len / 1024) <= 16131 partial rows,
+ * e.g. batch 16 with 32 heads up to 31744 keys) returns KB_ATTN_ERR_SCRATCH
+ * and launches nothing.  Every call on one GPU shares the array and it keeps
+ * the last call's contents (no call depends on them: each partial is written
+ * before it is read): calls whose work may overlap on one GPU (several
+ * streams, several host threads) race and must be serialised by the caller.
+ * Output bits are those of kb_attn_decode.  Other arguments and rules as for
+ * kb_attn_decode.
+ */
+int kb_attn_decode_static(const void* q, const void* k_cache, const void* v_cache, void* o,
+                          int64_t batch, int64_t kv_len, int64_t kv_capacity, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t head_dim, float scale, hipStream_t stream);
 
 /*
  * Decode of the last n_rows tokens (1 <= n_rows <= 8, else

@@ -11,7 +11,7 @@ import bitwise_aligned_causal_amd as kb
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kb_attn.h")
 
-OK, INVALID, UNSUPPORTED, LENGTH, ALIGN, DEVICE, WORKSPACE, ALIAS, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, INVALID, UNSUPPORTED, LENGTH, ALIGN, DEVICE, WORKSPACE, ALIAS, HIP, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 SCALE = 128 ** -0.5
 
 # fake, aligned, non-overlapping "device" addresses: every call below must
@@ -77,7 +77,14 @@ def decode(**kw):
                                    a["hkv"], a["d"], a["scale"], a["ws"], a["ws_bytes"], None)
 
 
-@pytest.mark.parametrize("call", [prefill, partitioned, decode])
+def decode_static(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, batch=1, kv_len=2048, cap=4096, hq=32, hkv=8, d=128, scale=SCALE)
+    a.update(kw)
+    return kb.lib().kb_attn_decode_static(a["q"], a["k"], a["v"], a["o"], a["batch"], a["kv_len"], a["cap"],
+                                          a["hq"], a["hkv"], a["d"], a["scale"], None)
+
+
+@pytest.mark.parametrize("call", [prefill, partitioned, decode, decode_static])
 @pytest.mark.parametrize("kw,expect", [
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
     (dict(batch=0), INVALID), (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID),
@@ -265,3 +272,27 @@ def test_decode_multi_workspace_bytes():
 ])
 def test_decode_multi_rejected_before_launch(kw, expect):
     assert decode_multi(**kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(kv_len=0), dict(kv_len=4097), dict(cap=(1 << 30) + 1)])
+def test_decode_static_lengths(kw):
+    assert decode_static(**kw) == LENGTH
+
+
+def test_decode_static_scratch_limit():
+    # 8 MiB holds 16131 partial rows of 130 floats: batch 1 with 32 heads fits
+    # 504 chunks.  At the limit the size check passes and the (fake) pointers
+    # fail the device check; one key more needs a 505th chunk and is refused
+    # for its size, before any device query.
+    limit = 504 * 1024
+    assert kb.decode_workspace_bytes(1, limit) <= kb.DECODE_STATIC_SCRATCH_BYTES
+    assert kb.decode_workspace_bytes(1, limit + 1) > kb.DECODE_STATIC_SCRATCH_BYTES
+    assert decode_static(kv_len=limit, cap=limit) == DEVICE
+    assert decode_static(kv_len=limit + 1, cap=limit + 1) == SCRATCH
+    assert decode_static(batch=16, kv_len=31 * 1024, cap=31 * 1024) == DEVICE
+    assert decode_static(batch=16, kv_len=31 * 1024 + 1, cap=32 * 1024) == SCRATCH
+    assert b"scratch" in kb.lib().kb_attn_strerror(SCRATCH)
+    # the header's size and the binding's agree
+    text = open(HEADER).read()
+    assert re.search(r"#define KB_ATTN_DECODE_STATIC_SCRATCH_BYTES \(8u << 20\)", text)
+    assert kb.DECODE_STATIC_SCRATCH_BYTES == 8 << 20
