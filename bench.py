@@ -109,12 +109,14 @@ def gpu_clocks() -> dict | None:
     return {k.strip(" :"): v for k, v in card.items() if "clk" in k.lower() or "clock" in k.lower()} or None
 
 
-def git_head() -> dict:
+def git_head(spawn: bool = True) -> dict:
     """The commit the tree comes from: git itself in a checkout, else the record
     the library build leaves beside libkb_attn.so (a copied tree has no .git)."""
     import subprocess
 
     try:
+        if not spawn or not os.path.isdir(os.path.join(ROOT, ".git")):
+            raise FileNotFoundError(".git")
         head = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
                               timeout=30)
         if head.returncode == 0:
@@ -654,8 +656,11 @@ def main() -> int:
         "kernel_source_hash": kernel_source_hash(),
         "inputs_sha256": {name: hashlib.sha256(np.ascontiguousarray(x).data).hexdigest()[:16]
                           for name, x in (("q", q), ("k", k), ("v", v))},
-        "env": {**device_env(torch, dev), "clocks_idle": gpu_clocks(), "clocks_busy": clocks_busy},
-        "git": git_head(),
+        "env": {**device_env(torch, dev), "clocks_idle": None if args.no_extras else gpu_clocks(),
+                "clocks_busy": clocks_busy},
+        # profiled runs (--no-extras) start no helper programs: the profiler's
+        # preloaded library would follow them
+        "git": git_head(spawn=not args.no_extras),
     }
     if not args.no_cpu_baseline:
         base, check = cpu_leg(q, k, v, out_pre, keep, sweep_cells, args.cpu_seconds, dev, torch)

@@ -46,6 +46,19 @@ def test_kernel_source_hash_is_stable():
     assert len(bench.kernel_source_hash()) == 16
 
 
+def test_git_record_without_helper_processes(monkeypatch):
+    """Profiled bench runs take the commit from the build record, never from git."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    def refuse(*a, **k):
+        raise AssertionError("subprocess started")
+
+    monkeypatch.setattr(subprocess, "run", refuse)
+    rec = bench.git_head(spawn=False)
+    assert rec["from"] in ("build record", "unavailable")
+
+
 def test_build_flags_that_the_kernels_rely_on():
     """The contract places every fused multiply-add explicitly (no contraction),
     packed fp32 arithmetic stays off, the code targets gfx950 only, and MFMA
