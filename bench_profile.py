@@ -124,26 +124,49 @@ def prefill_wave_tiles() -> int:
     return bench.B * (bench.HQ // 4) * (blocks * (blocks + 1) // 2) * 8
 
 
-def sq_summary(dirs, out: str, src_hash: str) -> None:
-    vals = {}
+def sq_summary(dirs, out: str, src_hash: str, kernel: str = "prefill_kernel<false>", kernels=None,
+               fname: str = "prefill_kernel_b16_s16384", title: str = f"full causal prefill B={bench.B} S={bench.S}",
+               run_args: str = "--steps 1 --warmup 0 --no-cpu-baseline --no-extras",
+               unit: tuple[str, int] | None = None) -> None:
+    """SQ / GRBM counters of one kernel, mean over its dispatches in each pass,
+    per dispatch, per MFMA instruction and (if given) per work unit."""
+    kernels = kernels or KERNELS
+    vals, durs = {}, []
     for d in dirs:
-        for name, rows in per_counter(d).items():
-            vals.update(rows)
-    tiles = prefill_wave_tiles()
-    lines = [f"# prefill_kernel<false> SQ and GRBM counters, B={bench.B} S={bench.S} ({tiles / 8:.3g} workgroup-tiles x 8 waves)",
+        for name, rows in per_counter(d, kernel, kernels).items():
+            vals[name] = statistics.mean(rows)
+    if unit is None and kernel == "prefill_kernel<false>":
+        unit = ("wave per 64-key tile", prefill_wave_tiles())
+    lines = [f"# {kernel} SQ and GRBM counters, {title}",
              f"kernel hash (code without comments, and compiler flags): {src_hash}", "",
              "commands (one pass each, counters split to stay within the SQ block limit):"]
-    lines += [f"  rocprofv3 --pmc {p} -d <dir> -o run --output-format csv -- "
-              "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extras" for p in SQ_PASSES]
-    lines += ["", "values for the full-prefill dispatch (SQ_WAVE_CYCLES and SQ_ACTIVE_* are in 4-cycle units):"]
-    lines += [f"  {k:<32} {v:>12.4g}   per wave per 64-key tile {v / tiles:>9.2f}" for k, v in sorted(vals.items())]
+    lines += [f"  rocprofv3 --pmc {p} -d <dir> -o run --output-format csv -- python3 bench.py {run_args}"
+              for p in SQ_PASSES]
+    head = f"  {'counter':<32} {'per dispatch':>12}   {'per MFMA':>9}"
+    if unit:
+        head += f"   per {unit[0]}"
+    lines += ["", "mean per dispatch (SQ_WAVE_CYCLES, SQ_BUSY_CU_CYCLES, SQ_WAIT_* and SQ_ACTIVE_* are in 4-cycle "
+                  "units; per MFMA = divided by SQ_INSTS_MFMA):", head]
+    mfma = vals.get("SQ_INSTS_MFMA")
+    for k, v in sorted(vals.items()):
+        row = f"  {k:<32} {v:>12.4g}   {v / mfma if mfma else float('nan'):>9.3f}"
+        if unit:
+            row += f"   {v / unit[1]:>9.2f}"
+        lines.append(row)
     if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "SQ_BUSY_CU_CYCLES" in vals:
         # MFMA busy cycles are summed over SIMDs, CU busy cycles over CUs (4 SIMDs each)
         util = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * vals["SQ_BUSY_CU_CYCLES"])
         lines += ["", f"MFMA utilisation: SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES) = {util:.3f} of the "
                       "SIMD cycles while the CUs are busy (at the clock the chip runs under this load)"]
+    if "SQ_WAIT_ANY" in vals and "SQ_WAVE_CYCLES" in vals:
+        lines += [f"waits: SQ_WAIT_ANY / SQ_WAVE_CYCLES = {vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.3f} of the "
+                  "wave cycles; SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES = "
+                  f"{vals.get('SQ_WAIT_INST_LDS', float('nan')) / vals['SQ_WAVE_CYCLES']:.3f}"]
+    if "SQ_INSTS_VALU" in vals and mfma:
+        lines += [f"VALU instructions (MFMA included) per MFMA: {vals['SQ_INSTS_VALU'] / mfma:.2f}; "
+                  f"transcendental per MFMA: {vals.get('SQ_INSTS_VALU_TRANS_F32', float('nan')) / mfma:.2f}"]
     if "GRBM_COUNT" in vals and "GRBM_GUI_ACTIVE" in vals:
-        dur = [d for name, rows in per_dispatch(dirs[-1]).items() if short(name) == "prefill_kernel<false>"
+        dur = [d for name, rows in per_dispatch(dirs[-1]).items() if short(name, kernels) == kernel
                for (_, _, _, d) in rows]
         if dur:
             sec = statistics.mean(dur) * 1e-9
@@ -151,16 +174,16 @@ def sq_summary(dirs, out: str, src_hash: str) -> None:
             lines += ["", f"clock under this load: GRBM_COUNT / (8 XCDs x dispatch time {sec * 1e3:.2f} ms) = "
                           f"{vals['GRBM_COUNT'] / (8 * sec) / 1e6:.0f} MHz; GRBM_GUI_ACTIVE / GRBM_COUNT = "
                           f"{vals['GRBM_GUI_ACTIVE'] / vals['GRBM_COUNT']:.3f}"]
-    with open(os.path.join(out, "prefill_kernel_b16_s16384_sq_counters.txt"), "w") as fh:
+    with open(os.path.join(out, f"{fname}_sq_counters.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
 
-def per_counter(d: str):
-    """{kernel: {counter: value}} for the full-prefill dispatch of one pass."""
+def per_counter(d: str, kernel: str, kernels):
+    """{counter: [value per dispatch of `kernel`]} of one pass."""
     out = {}
     for r in csv.DictReader(open(find_csv(d, "counter_collection.csv"))):
-        if short(r["Kernel_Name"]) == "prefill_kernel<false>":
-            out.setdefault("prefill_kernel<false>", {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        if short(r["Kernel_Name"], kernels) == kernel:
+            out.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     return out
 
 
@@ -226,6 +249,8 @@ def main():
     for a in ("stats", "fetch", "write", "copy_fetch", "copy_write", "out"):
         ap.add_argument("--" + a.replace("_", "-"), required=True)
     ap.add_argument("--sq", nargs="*", default=[], help="directories of the SQ counter passes")
+    ap.add_argument("--bwd-sq", nargs="*", default=[],
+                    help="directories of the SQ counter passes over bench.py --backward-only 3")
     for a in ("bwd_stats", "bwd_fetch", "bwd_write"):
         ap.add_argument("--" + a.replace("_", "-"), default=None,
                         help="rocprofv3 output of bench.py --backward-only 3 (stats, FETCH_SIZE, WRITE_SIZE)")
@@ -253,6 +278,9 @@ def main():
                         f_write, bench.backward_source_hash(), args.out, BWD_ARGS, BWD_ARGS, bwd_flops())
     if args.sq:
         sq_summary(args.sq, args.out, src_hash)
+    for k in ("bwd_dkdv_kernel", "bwd_dq_kernel") if args.bwd_sq else ():
+        fname, what = BWD_KERNELS[k]
+        sq_summary(args.bwd_sq, args.out, bench.backward_source_hash(), k, BWD_KERNELS, fname, what, BWD_ARGS)
 
 
 if __name__ == "__main__":
