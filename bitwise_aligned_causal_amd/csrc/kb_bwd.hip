@@ -9,15 +9,16 @@
 // on the inputs:
 //
 //   bwd_prep_kernel  D_i = <dO_i, O_i> and lse2_i = lse_i * log2(e) per row
-//   bwd_dkdv_kernel  two waves per 32 keys of a KV head (192 keys, 12 waves
-//                    per workgroup); the Q / dO rows of
-//                    the 4 query heads stream through LDS in 32-row tiles:
+//   bwd_dkdv_kernel  one wave per 32 keys of a KV head (256 keys, 8 waves
+//                    per workgroup; the block's V rows stay in LDS); the
+//                    Q / dO rows of the 4 query heads stream through LDS in
+//                    32-row tiles, and each wave computes for its keys
 //                      S    = Q K^T           (A = Q rows,  B = K rows in registers)
-//                      P    = exp2(S c - lse2),  dV^T += dO^T P        (first wave)
-//                      dP   = dO V^T          (A = dO rows, B = V rows in registers)
-//                      dS   = P (dP - D),  dK^T += Q^T dS            (second wave)
-//                    (the second operands read transposed from LDS; P passes
-//                    from the first wave to the second through LDS)
+//                      dP   = dO V^T          (A = dO rows, B = V rows from LDS)
+//                      P    = exp2(S c - lse2),  dS = P (dP - D)
+//                      dV^T += dO^T P,  dK^T += Q^T dS
+//                    (the last two with their first operands read
+//                    transposed from LDS)
 //   bwd_dq_kernel    one wave per 32 query rows; K / V tiles of 64 keys stream
 //                    through LDS as in the forward:
 //                      S^T  = K Q^T,  dP^T = V dO^T,  dQ^T += K^T dS^T
@@ -35,37 +36,49 @@ namespace kb {
 namespace bwd {
 
 // ---------------------------------------------------------------------------
-// LDS tiles: rows of 256 bytes (128 bf16), 16-byte chunk c of row r stored at
-// chunk position c ^ swz(r).  Tiles read both by rows and transposed use
-//   dual(r) = ((r & 3) << 2) | ((r >> 2) & 3)
-// which gives 16 distinct positions for the row reads (16 consecutive rows,
-// one chunk) and for the transposing reads (4 consecutive rows x 4
-// consecutive chunks); tiles read only by rows use r & 15.
+// LDS tiles: rows of 272 bytes (256 of data, 16 of padding that nothing
+// reads), the tile's row r stored at tile row
+//   prow(r) = 16 (r >> 4) + 4 (r & 3) + ((r >> 2) & 3)
+// (the two 2-bit fields of r swapped within each group of 16 rows, so prow
+// is its own inverse).  The row stride is 16 bytes past a multiple of 256,
+// so tile row t starts at bank group t mod 16:
+//   row reads (16 lanes: 16 consecutive rows, one 16-byte chunk) meet 16
+//     distinct tile rows mod 16, hence 16 distinct bank groups;
+//   transposing reads (32 lanes: the 4 rows 4m .. 4m + 3, 64 bytes each)
+//     meet tile rows 4n + (m mod 4), whose starts lie 64 bytes apart.
+// Every fragment address is a per-lane base plus an immediate offset.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int dual_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+constexpr int kRowBytes = 272;
 
-template <bool kDual>
-__device__ __forceinline__ int swz(int row) {
-    return kDual ? dual_swz(row) : (row & 15);
+__device__ __forceinline__ int prow(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// A tile of R rows: R * 17 slots of 16 bytes filled by whole one-KiB direct
+// loads (the last load of a 32-row tile runs into the tile's spare bytes).
+template <int R>
+struct PermTile {
+    static constexpr int kLoads = (R * 17 + 63) / 64;
+    static constexpr int kBytes = kLoads * 1024;
+};
+
+// Source byte offset, from the tile's first row, of direct load i, lane
+// `lane`: slot 64 i + lane is chunk c of tile row t, i.e. chunk min(c, 15) of
+// row prow(t).  Rows beyond min(last, R - 1) read that row instead (they are
+// masked or weighted by zero later; the padding chunk is never read).
+template <int R>
+__device__ __forceinline__ uint32_t perm_src(int i, int lane, int64_t last) {
+    const int p = 64 * i + lane;
+    const int t = p / 17, c = p - 17 * t;
+    const int64_t lim = last < R - 1 ? last : R - 1;
+    const int64_t r = prow(t) < lim ? prow(t) : lim;
+    return (uint32_t)(r * 256 + (c < 16 ? c : 15) * 16);
 }
 
-// Direct-to-LDS loads of a tile of 64 rows row0 .. row0 + 63 of a [rows, 128]
-// bf16 matrix; rows beyond last_row read last_row (they are masked or
-// weighted by zero later).  Instruction i (0..15) fills tile rows 4i .. 4i + 3,
-// lane L landing at tile byte 1024 i + 16 L; the wave issues instructions
-// first, first + step, ... (a rolled loop: it keeps no per-instruction
-// addresses live across the caller's loop).
-template <bool kDual>
-__device__ __forceinline__ void stage_rows(const uint16_t* base, int64_t row0, int64_t last_row, char* tile,
-                                           int first, int step, int lane) {
-    const char* tb = reinterpret_cast<const char*>(base + row0 * kHeadDim);
-    const int64_t last = last_row - row0;
-    for (int i = first; i < 16; i += step) {
-        const int row = 4 * i + (lane >> 4);
-        const int c = (lane & 15) ^ swz<kDual>(row);
-        const int64_t r = row < last ? row : last;
-        lds_dma16(tb, (uint32_t)(r * 256 + c * 16), tile + 1024 * i);
-    }
+// A planned offset (for a tile whose rows all lie inside the sequence)
+// re-aimed at row `last` when its row lies beyond it: the row is off >> 8 and
+// the chunk offset off & 255.
+__device__ __forceinline__ uint32_t clamp_src(uint32_t off, int64_t last) {
+    const int64_t r = off >> 8;
+    return r > last ? (uint32_t)(last * 256) + (off & 255u) : off;
 }
 
 // lds_dma16 with the scalar base forced into scalar registers: the base is
@@ -77,31 +90,40 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, char* dst
     lds_dma16(reinterpret_cast<const char*>((uintptr_t)(((uint64_t)hi << 32) | lo)), voff, dst);
 }
 
-// Row fragment: lane (row 32 blk + (lane & 31), half h) holds bf16
-// [16 st + 8h, 16 st + 8h + 7] of its row -- the A operand of a product whose
-// rows are the tile's rows, or the B operand whose columns are.
-template <bool kDual>
-__device__ __forceinline__ bf16x8 row_frag(const char* tile, int blk, int st, int lane) {
-    const int row = 32 * blk + (lane & 31);
-    const int c = 2 * st + (lane >> 5);
-    return lds_read16(tile + row * 256 + ((c ^ swz<kDual>(row)) << 4));
+// The LDS byte address of a pointer into a __shared__ array (the low 32 bits
+// of its generic address), as an LDS pointer: fragment addresses built on it
+// keep their constant parts as instruction offsets.
+typedef __attribute__((address_space(3))) const char lds_byte;
+__device__ __forceinline__ lds_byte* to_lds(const char* p) {
+    return (lds_byte*)(uintptr_t)(uint32_t)(uintptr_t)p;
 }
 
-// Transposed fragment (dual swizzle): the A operand X^T[d][rows] for d block
-// dblk and the 16-row step (blk, u) of the tile, with the row order of an
-// MFMA result column: lane (d = 32 dblk + j, half h) holds, in slot order,
+// Row fragment: lane (row 32 blk + (lane & 31), half h) holds bf16
+// [16 st + 8h, 16 st + 8h + 7] of its row -- the A operand of a product whose
+// rows are the tile's rows, or the B operand whose columns are.  `rb` is
+// row_base(lane) (prow(32 blk + i) = 32 blk + prow(i)).
+__device__ __forceinline__ int row_base(int lane) { return prow(lane & 31) * kRowBytes + (lane >> 5) * 16; }
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int rb, int blk, int st) {
+    const lds_byte* p = to_lds(tile) + rb + blk * 32 * kRowBytes + st * 32;
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p));
+}
+
+// Transposed fragment: the A operand X^T[d][rows] for d block dblk and the
+// 16-row step (blk, u) of the tile, with the row order of an MFMA result
+// column: lane (d = 32 dblk + j, half h) holds, in slot order,
 //   X[R0 + 4h + {0..3}][d], X[R0 + 8 + 4h + {0..3}][d],   R0 = 32 blk + 16 u
-// (two ds_read_b64_tr_b16; same addressing as the forward's V^T reads).
-__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int blk, int u, int dblk, int lane) {
+// (two ds_read_b64_tr_b16).  Lane (g = lane >> 4, n = (lane >> 2) & 3,
+// jj = lane & 3) points at row R0 + 4 (g >> 1) + n, tile row
+// R0 + 4n + (g >> 1), and d = 32 dblk + 16 (g & 1) + 4 jj; the second read is
+// 8 rows on, 2 tile rows on.  `tb` is tr_base(lane).
+__device__ __forceinline__ int tr_base(int lane) {
     const int g = lane >> 4, n = (lane >> 2) & 3, jj = lane & 3;
-    const int row0 = 32 * blk + 16 * u + 4 * (g >> 1) + n;
-    const int d = 32 * dblk + 16 * (g & 1) + 4 * jj;
-    const int c = d >> 3, half = (d & 4) << 1;
-    const int row1 = row0 + 8;
-    const char* p0 = tile + row0 * 256 + ((c ^ dual_swz(row0)) << 4) + half;
-    const char* p1 = tile + row1 * 256 + ((c ^ dual_swz(row1)) << 4) + half;
+    return (4 * n + (g >> 1)) * kRowBytes + 32 * (g & 1) + 8 * jj;
+}
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int tb, int blk, int u, int dblk) {
+    const lds_byte* p0 = to_lds(tile) + tb + (32 * blk + 16 * u) * kRowBytes + 64 * dblk;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * kRowBytes));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 all = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, all);
@@ -192,7 +214,7 @@ __device__ __forceinline__ BwdSeq dense_seq(const BwdArgs& a, int b) {
 
 // Ragged launches: at most kBwdMaxSeqs sequences, each padded to a multiple
 // of 64 rows in the workspace; unit_kv / unit_dq are the prefix sums of the
-// dK/dV and dQ work units (KV heads x 192-key blocks, KV heads x 64-row
+// dK/dV and dQ work units (KV heads x 256-key blocks, KV heads x 64-row
 // blocks) of the sequences in this launch.
 constexpr int kBwdMaxSeqs = 64;
 struct BwdTable {
@@ -272,76 +294,98 @@ __global__ __launch_bounds__(256) void bwd_prep_varlen_kernel(BwdArgs a, BwdTabl
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 12 waves on 192 keys [K0, K0 + 192) of one (sequence,
-// KV head).  Key group kg = w % 6 covers keys k0 = K0 + 32 kg .. + 31 and is
-// served by two waves:
-//   P-wave  (w < 6)   S = Q K^T, P = exp2(S c - lse2), P to LDS, dV^T += dO^T P
-//   dS-wave (w >= 6)  one item later: dP = dO V^T, P from LDS,
-//                     dS = P (dP - D), dK^T += Q^T dS
-// so each wave holds one accumulator set (64 registers) and one of K, V, and
-// fits in the 168 registers that let three waves share a SIMD.
+// dK, dV: workgroup = 8 waves on 256 keys [K0, K0 + 256) of one (sequence,
+// KV head).  Wave w owns keys k0 = K0 + 32 w .. + 31: it holds their K and V
+// rows as B operands and their dK^T and dV^T accumulators, and per work item
+// (32 query rows q0 .. q0 + 31 of one query head) computes
+//   S  = Q K^T,  dP = dO V^T                (A = Q / dO rows from LDS)
+//   P  = exp2(S c - lse2), masked on edge tiles;  dS = P (dP - D)
+//   dV^T += dO^T P,  dK^T += Q^T dS         (A = dO^T / Q^T from LDS)
 // Work items t = 0, 1, ...: query tile q0 = qlast - 32 (t / 4) of query head
-// 4g + (t % 4), from the last tile qlast down to K0.  A 4-stage LDS ring holds
-// each item's Q rows, dO rows (dual swizzle) and its 32 lse2 and 32 D values,
-// loaded two items ahead; P goes through a double buffer.  dK^T and dV^T
-// accumulate over the items in that fixed order.
+// 4g + (t % 4), from the last tile qlast down to K0; a wave skips the items
+// whose rows all precede its keys.  A 3-stage LDS ring holds each item's Q
+// and dO rows and its 32 lse2 and 32 D values, loaded two items ahead.  dK^T
+// and dV^T accumulate over the items in that fixed order.
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 12;
-constexpr int kKvGroups = 6;
-constexpr int kKvKeys = 32 * kKvGroups;
-constexpr int kQTileBytes = 32 * 256;
+constexpr int kKvWaves = 8;
+constexpr int kKvKeys = 32 * kKvWaves;
+constexpr int kQTileBytes = PermTile<32>::kBytes;     // 9 KiB
+constexpr int kKvTileLoads = PermTile<32>::kLoads;    // 9
 constexpr int kKvStageBytes = 2 * kQTileBytes + 256;  // Q, dO, lse2[32], D[32]
-constexpr int kKvStages = 4;
-constexpr int kPBufBytes = kKvGroups * 4096;          // fp32 P of the key groups
-constexpr int kKvLoadsPerWave = 3;  // waves 0..7: 2 tile loads + 1 block of 8 floats; waves 8..11: none
+constexpr int kKvStages = 3;
+// the workgroup's 256 V rows stay in LDS (a permuted padded tile) after the ring
+constexpr int kKvVBytes = PermTile<kKvKeys>::kBytes;  // 68 KiB
+constexpr int kKvVLoads = PermTile<kKvKeys>::kLoads;  // 68
+// a stage is 2 x 9 tile loads and two loads of 32 floats (lse2, D); wave w
+// issues loads w, w + 8, w + 16: waves 0..3 three per stage, waves 4..7 two
+constexpr int kKvStageLoads = 2 * kKvTileLoads + 2;
+constexpr int kKvLoadsMax = (kKvStageLoads + kKvWaves - 1) / kKvWaves;
+
+// Per-lane source offsets of this wave's tile loads for a tile whose 32 rows
+// all lie inside the sequence.
+struct KvPlan {
+    uint32_t o[kKvLoadsMax];
+    __device__ uint32_t off(int k) const { return o[k]; }
+};
 
 __device__ __forceinline__ void kv_stage(const BwdArgs& a, const BwdSeq& sq, int g, int t, int64_t qlast,
-                                         char* stage, int w, int lane) {
+                                         const KvPlan& plan, char* stage, int w, int lane) {
     const int64_t q0 = qlast - 32 * (t >> 2);
     const int64_t hh = kGroup * g + (t & 3);  // query head of the item
     const int64_t qrow = hh * sq.hstride + sq.q_row0 + q0;
     const char* qb = reinterpret_cast<const char*>(a.q + qrow * kHeadDim);
     const char* db = reinterpret_cast<const char*>(a.dout + qrow * kHeadDim);
     const int64_t last = sq.S - 1 - q0;  // last valid row, relative to q0
-    // waves 0..7 issue the stage's loads (waves 8..11 none): instructions 0..7
-    // fill Q rows 4i..4i+3, 8..15 fill dO; wave w issues w and w + 8
-    if (w >= 8) return;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int i = w + 8 * k;
-        const int row = 4 * (i & 7) + (lane >> 4);
-        const int c = (lane & 15) ^ dual_swz(row);
-        const int64_t r = row < last ? row : last;
-        dma16(i < 8 ? qb : db, (uint32_t)(r * 256 + c * 16), stage + 1024 * i);
+    for (int k = 0; k < kKvLoadsMax; ++k) {
+        const int i = w + kKvWaves * k;
+        if (i >= kKvStageLoads) break;
+        if (i < 2 * kKvTileLoads) {
+            const bool dO = i >= kKvTileLoads;
+            const int ti = dO ? i - kKvTileLoads : i;
+            const uint32_t o = plan.off(k);
+            const uint32_t off = last >= 31 ? o : clamp_src(o, last);
+            dma16(dO ? db : qb, off, stage + (dO ? kQTileBytes : 0) + 1024 * ti);
+        } else if (lane < 8) {
+            // lse2 (load 18) or D (load 19) of the 32 rows, 16 bytes a lane;
+            // padded arrays, in bounds
+            const bool dl = i > 2 * kKvTileLoads;
+            const float* src = (dl ? a.ws_d : a.ws_lse2) + hh * sq.ws_hstride + sq.ws_row0 + q0;
+            dma16(reinterpret_cast<const char*>(src), (uint32_t)(16 * lane), stage + 2 * kQTileBytes + (dl ? 128 : 0));
+        }
     }
-    // lse2 / D of the 32 rows (padded arrays, in bounds): wave w moves 8
-    // floats with lanes 0..1 (w < 4: lse2[8w ..], else D[8(w-4) ..])
-    const float* src = (w < 4 ? a.ws_lse2 : a.ws_d) + hh * sq.ws_hstride + sq.ws_row0 + q0 + 8 * (w & 3);
-    if (lane < 2) dma16(reinterpret_cast<const char*>(src), (uint32_t)(lane * 16), stage + 2 * kQTileBytes + 32 * w);
 }
 
-// Everything a dK/dV wave needs once its work item is known.
-struct KvWork {
-    BwdSeq sq;
-    int g;
-    int64_t S, K0, k0, qlast;
-    int n_items, kg, w, lane;
-    char* smem;
-    char* pbuf;
-};
-
-// P-wave part of one item: S = Q K^T, P (masked on edge tiles), P to LDS,
-// dV^T += dO^T P.  Element v: query q0 + 8 (v >> 2) + 4h + (v & 3), key
-// k0 + j; on an edge tile it counts when k0 + j <= query < S, i.e.
-// lo <= 8 (v >> 2) + (v & 3) < hi.  The mask is a uniform branch around the
-// selects only, so the accumulators never cross a join.
-__device__ __forceinline__ void p_item(const bf16x8 (&kf)[8], const char* sQ, const char* sD, const float* sL,
-                                       float4* pb4, int lane, float c, bool edge, int lo, int hi,
-                                       f32x16 (&acc)[4]) {
+// One work item of a wave.  Element v of an MFMA result: query
+// q0 + 8 (v >> 2) + 4h + (v & 3), key k0 + j; on an edge tile it counts when
+// k0 + j <= query < S, i.e. lo <= 8 (v >> 2) + (v & 3) < hi.  The mask is a
+// uniform branch around the selects only, so the accumulators never cross a
+// join.
+__device__ __forceinline__ void kv_item(const bf16x8 (&kf)[8], const char* sVw, const char* sQ,
+                                        const char* sD, const float* sL, int lane, int rb, int tb, float c,
+                                        bool edge, int lo, int hi, f32x16 (&acck)[4], f32x16 (&accv)[4]) {
     const int h = lane >> 5;
-    f32x16 s = zero16();
+    f32x16 s = zero16(), dp = zero16();
+    // the two products side by side, the Q and dO fragments read two steps
+    // ahead of their products and the V fragments one (scheduling fences keep
+    // this order: left alone, the compiler reads every fragment first and
+    // runs out of registers)
+    bf16x8 aq[3], ad[3], bv[2];
+    aq[0] = row_frag(sQ, rb, 0, 0);
+    ad[0] = row_frag(sD, rb, 0, 0);
+    bv[0] = row_frag(sVw, rb, 0, 0);
+    aq[1] = row_frag(sQ, rb, 0, 1);
+    ad[1] = row_frag(sD, rb, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) s = mfma(row_frag<true>(sQ, 0, st, lane), kf[st], s);
+    for (int st = 0; st < 8; ++st) {
+        if (st + 1 < 8) bv[(st + 1) % 2] = row_frag(sVw, rb, 0, st + 1);
+        if (st + 2 < 8) aq[(st + 2) % 3] = row_frag(sQ, rb, 0, st + 2);
+        s = mfma(aq[st % 3], kf[st], s);
+        if (st + 2 < 8) ad[(st + 2) % 3] = row_frag(sD, rb, 0, st + 2);
+        dp = mfma(ad[st % 3], bv[st % 2], dp);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int b4 = 0; b4 < 4; ++b4) {
         const float4 l2 = *reinterpret_cast<const float4*>(sL + 8 * b4 + 4 * h);
@@ -357,136 +401,120 @@ __device__ __forceinline__ void p_item(const bf16x8 (&kf)[8], const char* sQ, co
         }
     }
 #pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4)
-        pb4[b4 * 64 + lane] = make_float4(s[4 * b4], s[4 * b4 + 1], s[4 * b4 + 2], s[4 * b4 + 3]);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const bf16x8 pb = pack8(s, u);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sD, 0, u, db, lane), pb, acc[db]);
-    }
-}
-
-// dS-wave part of one item: dP = dO V^T, P from LDS, dS = P (dP - D),
-// dK^T += Q^T dS.
-__device__ __forceinline__ void ds_item(const bf16x8 (&vf)[8], const char* sQ, const char* sD, const float* sL,
-                                        const float4* pb4, int lane, f32x16 (&acc)[4]) {
-    const int h = lane >> 5;
-    f32x16 dp = zero16();
-#pragma unroll
-    for (int st = 0; st < 8; ++st) dp = mfma(row_frag<true>(sD, 0, st, lane), vf[st], dp);
-#pragma unroll
     for (int b4 = 0; b4 < 4; ++b4) {
-        const float4 p4 = pb4[b4 * 64 + lane];
         const float4 d4 = *reinterpret_cast<const float4*>(sL + 32 + 8 * b4 + 4 * h);
-        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dp[4 * b4 + i] = pv[i] * (dp[4 * b4 + i] - dv[i]);
+        for (int i = 0; i < 4; ++i) dp[4 * b4 + i] = s[4 * b4 + i] * (dp[4 * b4 + i] - dv[i]);
     }
+    const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
+    const bf16x8 sb[2] = {pack8(dp, 0), pack8(dp, 1)};
+    // the second products, their transposed fragments read one step ahead
+    bf16x8 td = tr_frag(sD, tb, 0, 0, 0), tq = tr_frag(sQ, tb, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const bf16x8 sb = pack8(dp, u);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sQ, 0, u, db, lane), sb, acc[db]);
+    for (int x = 0; x < 8; ++x) {
+        const int u = x >> 2, db = x & 3;
+        bf16x8 nd, nq;
+        if (x + 1 < 8) nd = tr_frag(sD, tb, 0, (x + 1) >> 2, (x + 1) & 3);
+        accv[db] = mfma(td, pb[u], accv[db]);
+        if (x + 1 < 8) nq = tr_frag(sQ, tb, 0, (x + 1) >> 2, (x + 1) & 3);
+        acck[db] = mfma(tq, sb[u], acck[db]);
+        __builtin_amdgcn_sched_barrier(0);
+        td = nd;
+        tq = nq;
     }
 }
 
-// The item loop of one role (both roles run the same iterations and
-// barriers; the P-wave works on item t, the dS-wave on item t - 1).  Each
-// role has its own loop so that its accumulators stay in place.
-template <bool kP>
-__device__ __forceinline__ void kv_loop(const BwdArgs& a, const KvWork& wk, const bf16x8 (&kvf)[8],
-                                        f32x16 (&acc)[4]) {
-    const int lane = wk.lane, j = lane & 31, h = lane >> 5;
-    const float c = a.c;
-    for (int t = 0; t <= wk.n_items; ++t) {
-        // publish item t's stage (the item t + 1 stage may still be loading), refill
-        if (t + 1 < wk.n_items)
-            wait_vm<kKvLoadsPerWave>();
-        else
-            wait_vm<0>();
-        __syncthreads();
-        if (t + 2 < wk.n_items)
-            kv_stage(a, wk.sq, wk.g, t + 2, wk.qlast, wk.smem + ((t + 2) % kKvStages) * kKvStageBytes, wk.w, lane);
-
-        const int it = kP ? t : t - 1;
-        if (it < 0 || it >= wk.n_items) continue;
-        const int64_t q0 = wk.qlast - 32 * (it >> 2);
-        if (q0 < wk.k0) continue;  // every key of this group lies after every row of the tile
-        const char* stage = wk.smem + (it % kKvStages) * kKvStageBytes;
-        const char* sQ = stage;
-        const char* sD = stage + kQTileBytes;
-        const float* sL = reinterpret_cast<const float*>(stage + 2 * kQTileBytes);
-        float4* pb4 = reinterpret_cast<float4*>(wk.pbuf + (it & 1) * kPBufBytes + wk.kg * 4096);
-        if (kP) {
-            const bool edge = q0 == wk.k0 || q0 + 32 > wk.S;
-            const int lo = (int)(wk.k0 - q0) + j - 4 * h;
-            const int hi = (int)(wk.S - q0 < 64 ? wk.S - q0 : 64) - 4 * h;
-            p_item(kvf, sQ, sD, sL, pb4, lane, c, edge, lo, hi, acc);
-        } else {
-            ds_item(kvf, sQ, sD, sL, pb4, lane, acc);
-        }
-    }
-}
-
-// One dK/dV workgroup: keys [192 kb, 192 kb + 192) of KV head g of one sequence.
+// One dK/dV workgroup: keys [256 kb, 256 kb + 256) of KV head g of one sequence.
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a, const BwdSeq& sq, int g, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kg = w % kKvGroups;
-    const bool pwave = w < kKvGroups;
     const int j = lane & 31, h = lane >> 5;
-    KvWork wk;
-    wk.sq = sq;
-    wk.g = g;
-    wk.S = sq.S;
-    wk.K0 = (int64_t)kb * kKvKeys;
-    wk.k0 = wk.K0 + 32 * kg;  // this wave's first key
+    const int64_t S = sq.S;
+    const int64_t K0 = (int64_t)kb * kKvKeys;
+    const int64_t k0 = K0 + 32 * w;  // this wave's first key
     // query tiles from the last one down to K0: every block of a (sequence,
     // KV head) starts at the same rows, so the blocks running together on an
     // XCD read the same Q / dO rows at about the same time (one L2 fetch)
-    wk.qlast = ((wk.S - 1) >> 5) << 5;
-    wk.n_items = 4 * (int)((wk.qlast - wk.K0) / 32 + 1);
-    wk.kg = kg;
-    wk.w = w;
-    wk.lane = lane;
-    wk.smem = smem;
-    wk.pbuf = smem + kKvStages * kKvStageBytes;
-    const int64_t S = wk.S;
-
-    kv_stage(a, sq, g, 0, wk.qlast, smem, w, lane);
-    if (wk.n_items >= 2) kv_stage(a, sq, g, 1, wk.qlast, smem + kKvStageBytes, w, lane);
-
-    // this wave's K (P-wave) or V (dS-wave) rows as B operands: lane (key j,
-    // half h) holds row k0 + j, d = 16 st + 8h .. + 7 (rows beyond S read row S - 1)
-    const int64_t kv0 = (int64_t)g * sq.hstride + sq.kv_row0;  // row of key 0
-    bf16x8 kvf[8];
-    {
-        int64_t key = wk.k0 + j;
-        key = key < S ? key : S - 1;
-        const uint16_t* src = (pwave ? a.k : a.v) + (kv0 + key) * kHeadDim;
+    const int64_t qlast = ((S - 1) >> 5) << 5;
+    const int n_items = 4 * (int)((qlast - K0) / 32 + 1);
+    const int rb = row_base(lane), tb = tr_base(lane);
+    KvPlan plan;
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
-            kvf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 16 * st + 8 * h));
+    for (int k = 0; k < kKvLoadsMax; ++k) {
+        const int i = w + kKvWaves * k;
+        const int ti = i < kKvTileLoads ? i : i - kKvTileLoads;
+        plan.o[k] = i < 2 * kKvTileLoads ? perm_src<32>(ti, lane, 31) : 0u;
     }
 
-    f32x16 acc[4];
+    const int64_t kv0 = (int64_t)g * sq.hstride + sq.kv_row0;  // row of key 0
+    char* sV = smem + kKvStages * kKvStageBytes;
+    {
+        // the block's V rows (rows beyond S read row S - 1)
+        const char* vb = reinterpret_cast<const char*>(a.v + (kv0 + K0) * kHeadDim);
+        for (int i = w; i < kKvVLoads; i += kKvWaves)
+            dma16(vb, perm_src<kKvKeys>(i, lane, S - 1 - K0), sV + 1024 * i);
+    }
+    kv_stage(a, sq, g, 0, qlast, plan, smem, w, lane);
+    if (n_items >= 2) kv_stage(a, sq, g, 1, qlast, plan, smem + kKvStageBytes, w, lane);
+
+    // this wave's K rows as B operands: lane (key j, half h) holds row k0 + j,
+    // d = 16 st + 8h .. + 7 (rows beyond S read row S - 1)
+    bf16x8 kf[8];
+    {
+        int64_t key = k0 + j;
+        key = key < S ? key : S - 1;
+        const uint16_t* ks = a.k + (kv0 + key) * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] = zero16();
-    const int64_t row = (kv0 + wk.k0 + j) * kHeadDim;
-    if (pwave) {
-        kv_loop<true>(a, wk, kvf, acc);
-        if (wk.k0 + j < S) store_col(a.dv + row, acc, 1.0f, h);
-    } else {
-        kv_loop<false>(a, wk, kvf, acc);
-        if (wk.k0 + j < S) store_col(a.dk + row, acc, a.scale, h);
+        for (int st = 0; st < 8; ++st)
+            kf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks + 16 * st + 8 * h));
+    }
+    // the fragments are complete before the item loop: otherwise the compiler
+    // keeps waits for them inside the loop, where they also hold each item
+    // behind the direct loads it has just issued
+    wait_vm<0>();
+
+    f32x16 acck[4], accv[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        acck[db] = zero16();
+        accv[db] = zero16();
+    }
+    const float c = a.c;
+    for (int t = 0; t < n_items; ++t) {
+        // publish item t's stage (the item t + 1 stage may still be loading), refill
+        if (t + 1 < n_items) {
+            if (w < kKvStageLoads - (kKvLoadsMax - 1) * kKvWaves)
+                wait_vm<kKvLoadsMax>();
+            else
+                wait_vm<kKvLoadsMax - 1>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads();
+        if (t + 2 < n_items)
+            kv_stage(a, sq, g, t + 2, qlast, plan, smem + ((t + 2) % kKvStages) * kKvStageBytes, w, lane);
+
+        const int64_t q0 = qlast - 32 * (t >> 2);
+        if (q0 < k0) continue;  // every key of this wave lies after every row of the tile
+        const char* stage = smem + (t % kKvStages) * kKvStageBytes;
+        const bool edge = q0 == k0 || q0 + 32 > S;
+        const int lo = (int)(k0 - q0) + j - 4 * h;
+        const int hi = (int)(S - q0 < 64 ? S - q0 : 64) - 4 * h;
+        kv_item(kf, sV + 32 * w * kRowBytes, stage, stage + kQTileBytes,
+                reinterpret_cast<const float*>(stage + 2 * kQTileBytes), lane, rb, tb, c, edge, lo, hi, acck, accv);
+    }
+    const int64_t row = (kv0 + k0 + j) * kHeadDim;
+    if (k0 + j < S) {
+        store_col(a.dv + row, accv, 1.0f, h);
+        store_col(a.dk + row, acck, a.scale, h);
     }
 }
 
 // Dense batch: [B, H, S, 128].
 __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + 2 * kPBufBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + kKvVBytes];
     const int n_kb = (int)((a.seq_len + kKvKeys - 1) / kKvKeys);
     const int nbg = a.batch * a.n_kv_heads;
     const int x = blockIdx.x;
@@ -504,10 +532,10 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(BwdArgs a) {
     dkdv_body(a, dense_seq(a, bg / a.n_kv_heads), bg % a.n_kv_heads, kb, smem);
 }
 
-// Ragged batch (packed [H, T, 128]): units of a sequence are (192-key block,
+// Ragged batch (packed [H, T, 128]): units of a sequence are (256-key block,
 // KV head), longest blocks first.
 __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_varlen_kernel(BwdArgs a, BwdTable t) {
-    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + 2 * kPBufBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kKvStages * kKvStageBytes + kKvVBytes];
     const int x = blockIdx.x;
     int s = 0;
     while (s + 1 < t.n_seqs && t.unit_kv[s + 1] <= x) ++s;
@@ -518,17 +546,39 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_varlen_kernel(BwdArgs 
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 8 waves = the 4 query heads of one KV head x 2 halves of
 // the 64 positions [64 pb, 64 pb + 64), as in the forward; K / V tiles of 64
-// keys (K dual-swizzled, V rows only) stream through a 3-stage ring, loads two
+// keys (K and V, permuted padded tiles) stream through a 3-stage ring, loads two
 // tiles ahead.  Wave column j is query row 64 pb + 32 (w >> 2) + j.
 // ---------------------------------------------------------------------------
 constexpr int kDqWaves = 8;
 constexpr int kDqStages = 3;
-constexpr int kDqLoadsPerWave = kTileLoads / kDqWaves;
+constexpr int kDqTileLoads = PermTile<64>::kLoads;  // 17
+constexpr int kDqTileBytes = PermTile<64>::kBytes;  // 17 KiB
+constexpr int kDqStageBytes = 2 * kDqTileBytes;     // K, V
+// a stage is 2 x 17 loads; wave w issues loads w, w + 8, ...: waves 0, 1
+// five per stage, waves 2..7 four
+constexpr int kDqStageLoads = 2 * kDqTileLoads;
+constexpr int kDqLoadsMax = (kDqStageLoads + kDqWaves - 1) / kDqWaves;
 
-__device__ __forceinline__ void dq_stage(const uint16_t* kb, const uint16_t* vb, int64_t key0, int64_t last,
-                                         char* stage, int w, int lane) {
-    stage_rows<true>(kb, key0, last, stage, w, kDqWaves, lane);
-    stage_rows<false>(vb, key0, last, stage + kKBytes, w, kDqWaves, lane);
+// Per-lane source offsets of this wave's loads for a tile whose 64 keys all
+// lie inside the sequence.
+struct DqPlan {
+    uint32_t off[kDqLoadsMax];
+};
+
+__device__ __forceinline__ void dq_stage(const uint16_t* kb, const uint16_t* vb, int64_t key0, int64_t S,
+                                         const DqPlan& plan, char* stage, int w, int lane) {
+    const char* kt = reinterpret_cast<const char*>(kb + key0 * kHeadDim);
+    const char* vt = reinterpret_cast<const char*>(vb + key0 * kHeadDim);
+    const int64_t last = S - 1 - key0;  // last valid key, relative to key0
+#pragma unroll
+    for (int k = 0; k < kDqLoadsMax; ++k) {
+        const int i = w + kDqWaves * k;
+        if (i >= kDqStageLoads) break;
+        const bool vtile = i >= kDqTileLoads;
+        const int ti = vtile ? i - kDqTileLoads : i;
+        const uint32_t off = last >= 63 ? plan.off[k] : clamp_src(plan.off[k], last);
+        dma16(vtile ? vt : kt, off, stage + (vtile ? kDqTileBytes : 0) + 1024 * ti);
+    }
 }
 
 // One dQ workgroup: positions [64 pb, 64 pb + 64) of the 4 query heads of KV
@@ -547,9 +597,17 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
     const uint16_t* kbase = a.k + ((int64_t)g * sq.hstride + sq.kv_row0) * kHeadDim;
     const uint16_t* vbase = a.v + ((int64_t)g * sq.hstride + sq.kv_row0) * kHeadDim;
     const int t_last = pb;
+    const int rb = row_base(lane), tb = tr_base(lane);
+    DqPlan plan;
+#pragma unroll
+    for (int k = 0; k < kDqLoadsMax; ++k) {
+        const int i = w + kDqWaves * k;
+        const int ti = i < kDqTileLoads ? i : i - kDqTileLoads;
+        plan.off[k] = i < kDqStageLoads ? perm_src<64>(ti, lane, 63) : 0u;
+    }
 
-    dq_stage(kbase, vbase, 0, S - 1, smem, w, lane);
-    if (t_last >= 1) dq_stage(kbase, vbase, kTile, S - 1, smem + kTileBytes, w, lane);
+    dq_stage(kbase, vbase, 0, S, plan, smem, w, lane);
+    if (t_last >= 1) dq_stage(kbase, vbase, kTile, S, plan, smem + kDqStageBytes, w, lane);
 
     // B operands of this wave's rows: Q and dO, lane (row j, half h) holds d = 16 st + 8h .. + 7
     bf16x8 qf[8], df[8];
@@ -570,6 +628,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
             Di = a.ws_d[wsrow0 + pos];
         }
     }
+    // complete before the tile loop (see dkdv_body)
+    wait_vm<0>();
 
     f32x16 acc[4];
 #pragma unroll
@@ -577,28 +637,45 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
     const float c = a.c;
 
     for (int t = 0; t <= t_last; ++t) {
-        if (t + 1 <= t_last)
-            wait_vm<kDqLoadsPerWave>();
-        else
+        if (t + 1 <= t_last) {
+            if (w < kDqStageLoads - (kDqLoadsMax - 1) * kDqWaves)
+                wait_vm<kDqLoadsMax>();
+            else
+                wait_vm<kDqLoadsMax - 1>();
+        } else {
             wait_vm<0>();
+        }
         __syncthreads();
         if (t + 2 <= t_last) {
-            char* nb = smem + ((t + 2) % kDqStages) * kTileBytes;
-            dq_stage(kbase, vbase, (int64_t)(t + 2) * kTile, S - 1, nb, w, lane);
+            char* nb = smem + ((t + 2) % kDqStages) * kDqStageBytes;
+            dq_stage(kbase, vbase, (int64_t)(t + 2) * kTile, S, plan, nb, w, lane);
         }
-        const char* sK = smem + (t % kDqStages) * kTileBytes;
-        const char* sV = sK + kKBytes;
+        const char* sK = smem + (t % kDqStages) * kDqStageBytes;
+        const char* sV = sK + kDqTileBytes;
         const int64_t key0 = (int64_t)t * kTile;
 
         f32x16 s[2], dp[2];
+        {
+            // the 32 products of S^T and dP^T, each pair's K and V fragments
+            // read two steps ahead (scheduling fences keep this order)
+            s[0] = zero16();
+            dp[0] = zero16();
+            s[1] = zero16();
+            dp[1] = zero16();
+            bf16x8 fk[3], fv[3];
+            fk[0] = row_frag(sK, rb, 0, 0);
+            fv[0] = row_frag(sV, rb, 0, 0);
+            fk[1] = row_frag(sK, rb, 0, 1);
+            fv[1] = row_frag(sV, rb, 0, 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = zero16();
-            dp[kb] = zero16();
-#pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                s[kb] = mfma(row_frag<true>(sK, kb, st, lane), qf[st], s[kb]);
-                dp[kb] = mfma(row_frag<false>(sV, kb, st, lane), df[st], dp[kb]);
+            for (int x = 0; x < 16; ++x) {
+                const int kb = x >> 3, st = x & 7;
+                if (x + 2 < 16) fk[(x + 2) % 3] = row_frag(sK, rb, (x + 2) >> 3, (x + 2) & 7);
+                s[kb] = mfma(fk[x % 3], qf[st], s[kb]);
+                if (x + 2 < 16) fv[(x + 2) % 3] = row_frag(sV, rb, (x + 2) >> 3, (x + 2) & 7);
+                dp[kb] = mfma(fv[x % 3], df[st], dp[kb]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -622,13 +699,19 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
 #pragma unroll
             for (int v = 0; v < 16; ++v) dp[kb][v] = s[kb][v] * (dp[kb][v] - Di);
         }
+        {
+            // dQ^T += K^T dS^T, the transposed K fragments read two steps ahead
+            const bf16x8 sb[4] = {pack8(dp[0], 0), pack8(dp[0], 1), pack8(dp[1], 0), pack8(dp[1], 1)};
+            bf16x8 ft[3];
+            ft[0] = tr_frag(sK, tb, 0, 0, 0);
+            ft[1] = tr_frag(sK, tb, 0, 0, 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8 sb = pack8(dp[kb], u);
-#pragma unroll
-                for (int db = 0; db < 4; ++db) acc[db] = mfma(tr_frag(sK, kb, u, db, lane), sb, acc[db]);
+            for (int x = 0; x < 16; ++x) {
+                const int ku = x >> 2, db = x & 3;  // ku = 2 kb + u
+                if (x + 2 < 16) ft[(x + 2) % 3] = tr_frag(sK, tb, (x + 2) >> 3, ((x + 2) >> 2) & 1, (x + 2) & 3);
+                acc[db] = mfma(ft[x % 3], sb[ku], acc[db]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -638,7 +721,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
 
 // Dense batch: [B, H, S, 128].
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kDqStageBytes];
     const int n_pb = (int)((a.seq_len + 63) / 64);
     const int nbg = a.batch * a.n_kv_heads;
     const int x = blockIdx.x;
@@ -658,7 +741,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdArgs a) {
 // Ragged batch (packed [H, T, 128]): units of a sequence are (64-row block,
 // KV head), longest blocks first.
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_varlen_kernel(BwdArgs a, BwdTable t) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kDqStages * kDqStageBytes];
     const int x = blockIdx.x;
     int s = 0;
     while (s + 1 < t.n_seqs && t.unit_dq[s + 1] <= x) ++s;
