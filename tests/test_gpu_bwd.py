@@ -88,7 +88,11 @@ def run_backward(q, k, v, do, seed_note=""):
     return o, lse, dq, dk, dv
 
 
-@pytest.mark.parametrize("B,S", [(1, 1), (1, 17), (2, 64), (1, 100), (1, 257), (2, 300), (1, 1024)])
+# 257, 513 and 800 end one key past, one key past two, and 32 keys into the
+# fourth of the dK/dV kernel's 256-key blocks (waves with no valid key, a
+# partial last 32-row tile)
+@pytest.mark.parametrize("B,S", [(1, 1), (1, 17), (2, 64), (1, 100), (1, 257), (2, 300), (1, 513), (1, 800),
+                                 (1, 1024)])
 def test_backward_matches_oracle(B, S):
     q, k, v, do = make(1000 + S, B, S)
     _, lse, dq, dk, dv = run_backward(q, k, v, do)
@@ -222,7 +226,7 @@ def test_backward_full_size_sampled():
     assert np.all(np.abs(sv - dos) <= 2.0 ** -6 * scale_v), "sum_j dV_j differs from the summed dO"
 
 
-@pytest.mark.parametrize("hq,hkv,S,scale", [(4, 1, 129, 0.05), (8, 2, 70, None), (12, 3, 257, 0.2)])
+@pytest.mark.parametrize("hq,hkv,S,scale", [(4, 1, 129, 0.05), (8, 2, 70, None), (12, 3, 257, 0.2), (4, 1, 600, 0.1)])
 def test_backward_other_heads_and_scale(hq, hkv, S, scale):
     m = kb()
     q = kb_gen.normal_bf16(300 + S, 1, (1, hq, S, D))
