@@ -421,8 +421,10 @@ __device__ __forceinline__ void kv_item(const bf16x8 (&kf)[8], const char* sVw, 
         if (x + 1 < 8) nq = tr_frag(sQ, tb, 0, (x + 1) >> 2, (x + 1) & 3);
         acck[db] = mfma(tq, sb[u], acck[db]);
         __builtin_amdgcn_sched_barrier(0);
-        td = nd;
-        tq = nq;
+        if (x + 1 < 8) {
+            td = nd;
+            tq = nq;
+        }
     }
 }
 
@@ -566,7 +568,7 @@ struct DqPlan {
 };
 
 __device__ __forceinline__ void dq_stage(const uint16_t* kb, const uint16_t* vb, int64_t key0, int64_t S,
-                                         const DqPlan& plan, char* stage, int w, int lane) {
+                                         const DqPlan& plan, char* stage, int w) {
     const char* kt = reinterpret_cast<const char*>(kb + key0 * kHeadDim);
     const char* vt = reinterpret_cast<const char*>(vb + key0 * kHeadDim);
     const int64_t last = S - 1 - key0;  // last valid key, relative to key0
@@ -606,8 +608,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
         plan.off[k] = i < kDqStageLoads ? perm_src<64>(ti, lane, 63) : 0u;
     }
 
-    dq_stage(kbase, vbase, 0, S, plan, smem, w, lane);
-    if (t_last >= 1) dq_stage(kbase, vbase, kTile, S, plan, smem + kDqStageBytes, w, lane);
+    dq_stage(kbase, vbase, 0, S, plan, smem, w);
+    if (t_last >= 1) dq_stage(kbase, vbase, kTile, S, plan, smem + kDqStageBytes, w);
 
     // B operands of this wave's rows: Q and dO, lane (row j, half h) holds d = 16 st + 8h .. + 7
     bf16x8 qf[8], df[8];
@@ -648,7 +650,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
         __syncthreads();
         if (t + 2 <= t_last) {
             char* nb = smem + ((t + 2) % kDqStages) * kDqStageBytes;
-            dq_stage(kbase, vbase, (int64_t)(t + 2) * kTile, S, plan, nb, w, lane);
+            dq_stage(kbase, vbase, (int64_t)(t + 2) * kTile, S, plan, nb, w);
         }
         const char* sK = smem + (t % kDqStages) * kDqStageBytes;
         const char* sV = sK + kDqTileBytes;
