@@ -41,8 +41,10 @@
  *     kv_len * 2^64 and kv_len * 2^64 * max|v|; the contract also needs
  *     kv_len * max|v| < 2^64 (|v| < 2^34 at the longest kv_len, 2^30).
  *   - The caller owns every buffer; the library allocates nothing, keeps no
- *     state and is thread-safe.  Calls are asynchronous on `stream` (0 = the
- *     null stream) and return once the work is enqueued.
+ *     state (except kb_attn_decode_static's per-GPU scratch, below) and is
+ *     thread-safe (kb_attn_decode_static calls that overlap on one GPU race
+ *     on that scratch).  Calls are asynchronous on `stream` (0 = the null
+ *     stream) and return once the work is enqueued.
  *   - o must not overlap any input.
  *   - Every argument is checked before anything is launched; on error nothing
  *     is launched and a negative KB_ATTN_ERR_* code is returned.
