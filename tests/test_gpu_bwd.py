@@ -268,3 +268,35 @@ def test_backward_from_partitioned_forward_is_bitwise_the_same():
     got = [bits(x) for x in m.backward(Q, K, V, o2, DO, lse2)]
     for name, a, b in zip(("dq", "dk", "dv"), got, ref):
         assert np.array_equal(a, b), name
+
+
+def test_backward_seeded_random_shapes():
+    """Eight seeded random shapes (B 1-2, Hkv 1-2, S 1-900, scale 0.03-0.2):
+    the gradients against the oracle's budgets, and a second call's bits equal
+    the first's."""
+    m = kb()
+    rng = np.random.default_rng(2024)
+    for case in range(8):
+        B = int(rng.integers(1, 3))
+        hkv = int(rng.integers(1, 3))
+        hq = 4 * hkv
+        S = int(rng.integers(1, 901))
+        sc = float(rng.uniform(0.03, 0.2))
+        seed = 500 + case
+        q = kb_gen.normal_bf16(seed, 1, (B, hq, S, D))
+        k = kb_gen.normal_bf16(seed, 2, (B, hkv, S, D))
+        v = kb_gen.normal_bf16(seed, 3, (B, hkv, S, D))
+        do = kb_gen.normal_bf16(seed, 4, (B, hq, S, D))
+        Q, K, V, DO = dev(q), dev(k), dev(v), dev(do)
+        what = f"case {case}: B={B} Hq={hq} Hkv={hkv} S={S} scale={sc:.4f}"
+        note(f"backward {what}")
+        o, lse = m.prefill_lse(Q, K, V, sc)
+        dq, dk, dv = m.backward(Q, K, V, o, DO, lse, sc)
+        first = [bits(x) for x in (dq, dk, dv)]
+        ref = oracle.backward(q, k, v, do, scale=sc, budgets=True, threads=oracle_threads())
+        check_grad(first[0], ref["dq"], ref["eq"], f"dq {what}")
+        check_grad(first[1], ref["dk"], ref["ek"], f"dk {what}")
+        check_grad(first[2], ref["dv"], ref["ev"], f"dv {what}")
+        again = [bits(x) for x in m.backward(Q, K, V, o, DO, lse, sc)]
+        for name, a, b in zip(("dq", "dk", "dv"), again, first):
+            assert np.array_equal(a, b), f"{name} {what}: a rerun changed bits"
