@@ -359,9 +359,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Scores of one tile and the tile's max over both key blocks (masked where
 // kMask: key j > pos gives -inf).  Block 0's chain is issued first and block
-// 1's after it, each fragment read four products ahead; block 0's mask and
-// max run between block 1's products.  The order is fixed with scheduling
-// fences.
+// 1's after it, each fragment read four products ahead, the order fixed with
+// scheduling fences.  Block 0's mask and max are written between block 1's
+// products, but the compiler reassociates the max tree (the max is exact in
+// any order) and issues it after the last product; held in place by empty
+// asm barriers it ran no faster.
 template <class L, bool kMask>
 __device__ __forceinline__ float qk_tile_max(const bf16x8 (&qf)[8], const char* sK, int lane, int64_t key0,
                                              int64_t pos, f32x16& s0, f32x16& s1) {
