@@ -45,7 +45,6 @@ struct PrefillArgs {
 };
 
 constexpr int kPrefillWaves = 8;
-constexpr int kStages = 3;
 
 // Everything a prefill workgroup needs once its work item is known.
 struct PrefillWork {
@@ -63,32 +62,45 @@ struct PrefillWork {
 // absolute positions [64 pb, 64 pb + 64).  Every row of the block has its last
 // visible key in tile pb, so all rows visit exactly the tiles 0..pb and never
 // a tile that is fully masked for them.  K/V tiles are shared by the 8 waves
-// through a 3-stage LDS ring (padded rows, PaddedTile) filled by direct loads two
-// tiles ahead.
+// through a 4-stage LDS ring (padded rows, PaddedTile) filled by direct loads.
 // kPartitioned = false is the full-sequence case (q_len == kv_len, row r at
 // position r); both instantiations run the same per-row arithmetic.
+//
+// Ping-pong: waves w and w + 4 share a SIMD.  Group 0 (waves 0-3) runs tile t
+// as products then softmax, group 1 (waves 4-7) one step behind as softmax of
+// tile t - 1 then products, so while one wave of a SIMD multiplies the other
+// runs its vector work:
+//   products(t)  P V of tile t - 1 (pv_fenced), then the scores of tile t
+//                (qk_fenced); wave priority 3, so its MFMAs issue first
+//   softmax(t)   softmax_tile of tile t at priority 0, after issuing this
+//                wave's share of the direct loads of tile t + 2
+// One barrier per tile: before the products of tile t every wave has waited
+// for its loads of tile t and is past all reads of tile t - 2, whose stage
+// tile t + 2 then takes.
+constexpr int kStages = 4;
+
 template <bool kPartitioned>
 __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = w >> 2;
     const int pb = wk.pb;
     const int j = lane & 31, h = lane >> 5;
 
     const int64_t off = kPartitioned ? wk.kv_len - wk.q_len : 0;
-    const int64_t pos = (int64_t)pb * 64 + 32 * (w >> 2) + j;
+    const int64_t pos = (int64_t)pb * 64 + 32 * grp + j;
     const int64_t r = pos - off;
     const bool active = r >= 0 && r < wk.q_len;
 
     const uint16_t* kbase = wk.kbase;
     const uint16_t* vbase = wk.vbase;
     const int64_t kv_len = wk.kv_len;
-    const int t_last = pb;
+    const int T = pb;  // the diagonal tile, the last one
 
     StagePlan<PaddedTile, kPrefillWaves> plan;
     stage_plan(plan, lane, w);
     stage_tile(plan, kbase, vbase, 0, kv_len, smem, lane, w);
-    if (t_last >= 1)
-        stage_tile(plan, kbase, vbase, kTile, kv_len, smem + PaddedTile::kBytes, lane, w);
+    if (T >= 1) stage_tile(plan, kbase, vbase, kTile, kv_len, smem + PaddedTile::kBytes, lane, w);
 
     const int64_t qrow0 = (int64_t)(w & 3) * wk.q_hstride;  // this wave's query head
     bf16x8 qf[8];
@@ -113,20 +125,6 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
         acc[db] = zero16();
     }
     bool have_total = false;
-
-    // Wait for this wave's loads of tile t, publish it to the workgroup, then
-    // start the loads of tile t + 2 into the stage nobody reads any more.
-    auto publish = [&](int t) {
-        if (t + 1 <= t_last)
-            wait_stage_loads<PaddedTile, kPrefillWaves>(w);
-        else
-            wait_vm<0>();
-        __syncthreads();
-        if (t + 2 <= t_last) {
-            char* nb = smem + ((t + 2) % kStages) * PaddedTile::kBytes;
-            stage_tile(plan, kbase, vbase, (int64_t)(t + 2) * kTile, kv_len, nb, lane, w);
-        }
-    };
     auto close_chunk = [&]() {
         if (!have_total) {
             Mc = mc;
@@ -151,32 +149,90 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
         for (int db = 0; db < 4; ++db) acc[db] = zero16();
     };
 
-    // tiles below the diagonal: every key visible to every row; chunk by
-    // chunk, the first tile of each peeled (it starts from zero accumulators)
-    for (int t0 = 0; t0 < t_last; t0 += kTilesPerChunk) {
-        {
-            publish(t0);
-            const char* buf = smem + (t0 % kStages) * PaddedTile::kBytes;
-            tile_step<PaddedTile, 4, false, true>(qf, buf, buf + PaddedTile::kKStage, lane, (int64_t)t0 * kTile, pos, c,
-                                                  mc, l, acc, 0);
+    // Start of tile t's products: this wave's loads of tile t are done (group
+    // 0 may still have those of tile t + 1 in flight, group 1 has not issued
+    // them yet), then the barrier.
+    auto tile_start = [&](int t) {
+        if (t <= T) {
+            if (t + 1 <= T && grp == 0)
+                wait_stage_loads<PaddedTile, kPrefillWaves>(w);
+            else
+                wait_vm<0>();
         }
-        const int t_end = min(t0 + kTilesPerChunk, t_last);
-        for (int t = t0 + 1; t < t_end; ++t) {
-            publish(t);
-            const char* buf = smem + (t % kStages) * PaddedTile::kBytes;
-            tile_step<PaddedTile, 4, false>(qf, buf, buf + PaddedTile::kKStage, lane, (int64_t)t * kTile, pos, c, mc, l,
-                                            acc, 0);
+        __syncthreads();
+    };
+    f32x16 s0, s1;
+    bf16x8 pf[2][2];
+    float a_pend = 1.0f;  // rescale factor of the tile whose row sum is still to be added
+    auto products = [&](int t) {
+        __builtin_amdgcn_s_setprio(3);
+        if (t >= 1) {
+            float rs = 0.0f;
+            pv_fenced_rs<PaddedTile, 4>(pf, smem + ((t - 1) % kStages) * PaddedTile::kBytes + PaddedTile::kKStage, lane,
+                                        acc, 0, rs);
+            float ls_lo, ls_hi;
+            halves(rs, ls_lo, ls_hi);
+            l = __builtin_fmaf(l, a_pend, ls_lo + ls_hi);
         }
-        if (t_end == t0 + kTilesPerChunk) close_chunk();
+        if (t <= T) qk_fenced<PaddedTile>(qf, smem + (t % kStages) * PaddedTile::kBytes, lane, s0, s1);
+    };
+    // the softmax of tile t < T; `first` on the first tile of a chunk
+    auto softmax = [&](int t, bool first) {
+        __builtin_amdgcn_s_setprio(0);
+        if (t + 2 <= T)
+            stage_tile(plan, kbase, vbase, (int64_t)(t + 2) * kTile, kv_len,
+                       smem + ((t + 2) % kStages) * PaddedTile::kBytes, lane, w);
+        softmax_tile<4, false>(s0, s1, lane, (int64_t)t * kTile, pos, c, mc, a_pend, acc, pf, first);
+    };
+    auto softmax_diag = [&](bool first) {
+        __builtin_amdgcn_s_setprio(0);
+        softmax_tile<4, true>(s0, s1, lane, (int64_t)T * kTile, pos, c, mc, a_pend, acc, pf, first);
+    };
+    // tiles below the diagonal chunk by chunk (the first tile of a chunk
+    // peeled: the previous chunk is closed before its softmax), then the
+    // diagonal tile T and the P V products of T
+    const bool diag_first = (T % kTilesPerChunk) == 0;
+    if (grp == 0) {
+        for (int t0 = 0; t0 < T; t0 += kTilesPerChunk) {
+            const int tend = min(t0 + kTilesPerChunk, T);
+            tile_start(t0);
+            products(t0);
+            if (t0 > 0) close_chunk();
+            softmax(t0, true);
+            for (int t = t0 + 1; t < tend; ++t) {
+                tile_start(t);
+                products(t);
+                softmax(t, false);
+            }
+        }
+        tile_start(T);
+        products(T);
+        if (diag_first && T > 0) close_chunk();
+        softmax_diag(diag_first);
+        tile_start(T + 1);
+        products(T + 1);
+    } else {
+        tile_start(0);
+        products(0);
+        for (int t0 = 0; t0 < T; t0 += kTilesPerChunk) {
+            const int tend = min(t0 + kTilesPerChunk, T);
+            tile_start(t0 + 1);
+            if (t0 > 0) close_chunk();
+            softmax(t0, true);
+            products(t0 + 1);
+            for (int t = t0 + 1; t < tend; ++t) {
+                tile_start(t + 1);
+                softmax(t, false);
+                products(t + 1);
+            }
+        }
+        tile_start(T + 1);
+        if (diag_first && T > 0) close_chunk();
+        softmax_diag(diag_first);
+        products(T + 1);
     }
-    // the diagonal tile t_last holds keys beyond some rows' positions
-    {
-        publish(t_last);
-        const char* buf = smem + (t_last % kStages) * PaddedTile::kBytes;
-        tile_step<PaddedTile, 4, true>(qf, buf, buf + PaddedTile::kKStage, lane, (int64_t)t_last * kTile, pos, c, mc, l,
-                                       acc, 0);
-        close_chunk();
-    }
+    close_chunk();
+    __builtin_amdgcn_s_setprio(0);
 
     if (active) {
         uint16_t* orow = wk.o0 + (qrow0 + r) * kHeadDim;

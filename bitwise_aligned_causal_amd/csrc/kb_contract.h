@@ -357,63 +357,6 @@ constexpr float kLazyTau = 64.0f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Scores of one tile and the tile's max over both key blocks (masked where
-// kMask: key j > pos gives -inf).  Block 0's chain is issued first and block
-// 1's after it, each fragment read four products ahead, the order fixed with
-// scheduling fences.  Block 0's mask and max are written between block 1's
-// products, but the compiler reassociates the max tree (the max is exact in
-// any order) and issues it after the last product; held in place by empty
-// asm barriers it ran no faster.
-template <class L, bool kMask>
-__device__ __forceinline__ float qk_tile_max(const bf16x8 (&qf)[8], const char* sK, int lane, int64_t key0,
-                                             int64_t pos, f32x16& s0, f32x16& s1) {
-    const int h = lane >> 5;
-    const float ninf = -__builtin_inff();
-    s0 = zero16();
-    s1 = zero16();
-    bf16x8 kf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kf[i] = L::k_frag(sK, 0, i, lane);
-    float c0 = 0.0f, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        if (i < 8)
-            s0 = mfma(kf[i & 3], qf[i & 7], s0);
-        else
-            s1 = mfma(kf[i & 3], qf[i & 7], s1);
-        if (i + 4 < 16) kf[i & 3] = L::k_frag(sK, (i + 4) >> 3, (i + 4) & 7, lane);
-        if (i == 9) {
-            if (kMask) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    s0[v] = kk > pos ? ninf : s0[v];
-                }
-            }
-            c0 = vmax(vmax(s0[0], s0[1]), s0[2]);
-            c1 = vmax(vmax(s0[3], s0[4]), s0[5]);
-        } else if (i == 10) {
-            c2 = vmax(vmax(s0[6], s0[7]), s0[8]);
-            c3 = vmax(vmax(s0[9], s0[10]), s0[11]);
-        } else if (i == 11) {
-            c0 = vmax(vmax(c0, s0[12]), s0[13]);
-            c1 = vmax(vmax(c1, s0[14]), s0[15]);
-        } else if (i == 12) {
-            c0 = vmax(vmax(c0, c1), vmax(c2, c3));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (kMask) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t kk = key0 + 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            s1[v] = kk > pos ? ninf : s1[v];
-        }
-    }
-    const float m1 = block_max(s1);
-    return vmax(c0, m1);
-}
-
 // o *= a.  o * 1 == o exactly, so skipping the multiply when no column of
 // the wave moved its reference max leaves every bit as it is.
 template <int NDB>
@@ -427,9 +370,8 @@ __device__ __forceinline__ void rescale_o(f32x16 (&o)[NDB], float a, bool any_gr
     }
 }
 
-// P of one 16-key step (kb, u): 8 exps and 4 paired converts; the step's 4
-// dot2 row-sum terms continue the lane's chain `acc`.
-__device__ __forceinline__ void p_step(const f32x16& s, int u, float c, float nmc, bf16x8& pf, float& acc) {
+// P of one 16-key step (kb, u): 8 exps and 4 paired converts to bf16.
+__device__ __forceinline__ void p_only(const f32x16& s, int u, float c, float nmc, bf16x8& pf) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         f32x2 pp;
@@ -438,9 +380,24 @@ __device__ __forceinline__ void p_step(const f32x16& s, int u, float c, float nm
         const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
         pf[e] = pb[0];
         pf[e + 1] = pb[1];
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    }
+}
+
+// The step's 4 dot2 row-sum terms (bf16 P pairs against (1, 1)) continue the
+// lane's chain `acc`.
+__device__ __forceinline__ void row_sum_dot2(const bf16x8& pf, float& acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pb = {pf[e], pf[e + 1]};
         acc = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, acc, false);
     }
+}
+
+// P of one 16-key step with its row-sum terms.
+__device__ __forceinline__ void p_step(const f32x16& s, int u, float c, float nmc, bf16x8& pf, float& acc) {
+    p_only(s, u, c, nmc, pf);
+    row_sum_dot2(pf, acc);
 }
 
 // o += P V for one 16-key step (kb, u) over the wave's NDB d blocks.
@@ -454,20 +411,83 @@ __device__ __forceinline__ void pv_step(const bf16x8& pf, const char* sV, int kb
     }
 }
 
-// One whole tile; kMask selects the masked form (needed only on a tile that
-// holds keys beyond some column's position): scores, mask, the lazy
-// reference-max update, then P one 16-key step at a time (p_step) so that a
-// step's P V products (pv_step) can run beside the next step's exponentials.
-// kFirst marks the first tile of a chunk (mc = -inf, l = 0, o = 0 on entry):
-// its reference max always moves and a = 0, and o * 0 = +0 = o, so the
-// rescale is skipped and the products start from a zero accumulator -- the
-// same bits as the general form.
-template <class L, int NDB, bool kMask, bool kFirst = false>
-__device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK, const char* sV, int lane,
-                                          int64_t key0, int64_t pos, float c, float& mc, float& l,
-                                          f32x16 (&o)[NDB], int dblk0) {
-    f32x16 s0, s1;
-    float mt = qk_tile_max<L, kMask>(qf, sK, lane, key0, pos, s0, s1);
+// ---------------------------------------------------------------------------
+// A tile in parts for the prefill, whose waves run one part while their SIMD
+// partner runs the other: qk_fenced (the score products), then softmax_tile
+// (mask, max, lazy reference update, P, rescale of o), then pv_fenced_rs
+// (the P V products and the row sum) in the next product phase.
+// ---------------------------------------------------------------------------
+// Score products of one tile: block 0's chain, then block 1's, each fragment
+// read four products ahead, the order fixed with scheduling fences (at most
+// four fragments live).
+template <class L>
+__device__ __forceinline__ void qk_fenced(const bf16x8 (&qf)[8], const char* sK, int lane, f32x16& s0, f32x16& s1) {
+    s0 = zero16();
+    s1 = zero16();
+    bf16x8 kf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kf[i] = L::k_frag(sK, 0, i, lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (i < 8)
+            s0 = mfma(kf[i & 3], qf[i & 7], s0);
+        else
+            s1 = mfma(kf[i & 3], qf[i & 7], s1);
+        if (i + 4 < 16) kf[i & 3] = L::k_frag(sK, (i + 4) >> 3, (i + 4) & 7, lane);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// P V products of one tile in pv_step's order (key steps (0,0), (0,1), (1,0),
+// (1,1), each over the d blocks), fragments read four products ahead behind
+// scheduling fences, with the tile's row sum: after each key step's second
+// product, that step's dot2 terms continue `acc` (in step order).  The dot2
+// runs on the matrix pipe: beside this wave's own products it costs a few
+// cycles, while beside the partner wave's products (in the softmax) it
+// stalls them.
+template <class L, int NDB>
+__device__ __forceinline__ void pv_fenced_rs(const bf16x8 (&pf)[2][2], const char* sV, int lane, f32x16 (&o)[NDB],
+                                             int dblk0, float& acc) {
+    constexpr int N = 4 * NDB;
+    constexpr int D = 4;
+    bf16x8 vf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) vf[i] = L::vt_frag(sV, (i / NDB) >> 1, (i / NDB) & 1, dblk0 + i % NDB, lane);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int step = i / NDB, db = i % NDB;
+        o[db] = mfma(vf[i % D], pf[step >> 1][step & 1], o[db]);
+        if (i + D < N) {
+            const int sn = (i + D) / NDB, dn = (i + D) % NDB;
+            vf[i % D] = L::vt_frag(sV, sn >> 1, sn & 1, dblk0 + dn, lane);
+        }
+        if (db == 1) row_sum_dot2(pf[step >> 1][step & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The softmax of a tile whose scores are in (s0, s1): mask (kMask: key j >
+// pos gives -inf), tile max, lazy reference update, P (pf) and the rescale
+// of o -- the rescale only when a column of the wave moved its reference (o *
+// 1 == o), and none on a chunk's first tile (`first`: mc = -inf, l = 0, o =
+// +0 on entry, so a = 0 and o * 0 = +0 = o).  The row sum comes later with
+// the P V products (pv_fenced_rs); a_out is the factor the caller applies to
+// l then: l = fma(l, a, sum).
+template <int NDB, bool kMask>
+__device__ __forceinline__ void softmax_tile(f32x16& s0, f32x16& s1, int lane, int64_t key0, int64_t pos, float c,
+                                             float& mc, float& a_out, f32x16 (&o)[NDB], bf16x8 (&pf)[2][2],
+                                             bool first) {
+    if (kMask) {
+        const int h = lane >> 5;
+        const float ninf = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
+            s0[v] = kk > pos ? ninf : s0[v];
+            s1[v] = kk + 32 > pos ? ninf : s1[v];
+        }
+    }
+    float mt = vmax(block_max(s0), block_max(s1));
     {
         float lo, hi;
         halves(mt, lo, hi);
@@ -481,40 +501,23 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&qf)[8], const char* sK,
     float a = 1.0f;
     if (any_grow) a = grow ? exp2_hw(mc - mcn) : 1.0f;
     const float nmc = -mcn;
-
-    bf16x8 pf[2][2];
-    float acc = 0.0f;  // this lane's row-sum chain over the tile's 16 dot2 terms
-    p_step(s0, 0, c, nmc, pf[0][0], acc);
-    if (kFirst) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] = zero16();
-    } else {
-        rescale_o<NDB>(o, a, any_grow);
-    }
-    pv_step<L, NDB>(pf[0][0], sV, 0, 0, lane, o, dblk0);
-    p_step(s0, 1, c, nmc, pf[0][1], acc);
-    pv_step<L, NDB>(pf[0][1], sV, 0, 1, lane, o, dblk0);
-    p_step(s1, 0, c, nmc, pf[1][0], acc);
-    pv_step<L, NDB>(pf[1][0], sV, 1, 0, lane, o, dblk0);
-    p_step(s1, 1, c, nmc, pf[1][1], acc);
-    pv_step<L, NDB>(pf[1][1], sV, 1, 1, lane, o, dblk0);
-
-    // the two lane halves of the column: (low + high)
-    float ls_lo, ls_hi;
-    halves(acc, ls_lo, ls_hi);
-    const float ls = ls_lo + ls_hi;
-    l = __builtin_fmaf(l, a, ls);
+    p_only(s0, 0, c, nmc, pf[0][0]);
+    p_only(s0, 1, c, nmc, pf[0][1]);
+    p_only(s1, 0, c, nmc, pf[1][0]);
+    p_only(s1, 1, c, nmc, pf[1][1]);
+    if (!first) rescale_o<NDB>(o, a, any_grow);
+    a_out = a;
     mc = mcn;
 }
 
 // ---------------------------------------------------------------------------
-// tile_step in parts without branches, for the decode, which computes the
+// A tile in parts without branches, for the decode, which computes the
 // scores of tile t + 1 beside the softmax and P V of tile t: qk_plain issues
 // the score products (chains of both key blocks interleaved); softmax_flat
 // does the mask, max, lazy reference update, P, row sum and rescale of o as
-// tile_step does, but always computes a and always multiplies o by it (o * 1
-// == o exactly, so the bits are those of tile_step); pv_plain issues the P V
-// products in pv_step's order.
+// softmax_tile does, but always computes a and always multiplies o by it (o *
+// 1 == o exactly, so the bits are those of softmax_tile); pv_plain issues the
+// P V products in pv_step's order.
 // ---------------------------------------------------------------------------
 template <class L>
 __device__ __forceinline__ void qk_plain(const bf16x8 (&qf)[8], const char* sK, int lane, f32x16& s0, f32x16& s1) {
