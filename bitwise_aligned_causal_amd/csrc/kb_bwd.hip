@@ -23,7 +23,9 @@
 //                    through LDS as in the forward:
 //                      S^T  = K Q^T,  dP^T = V dO^T,  dQ^T += K^T dS^T
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS
-// are rounded to bf16 (RNE) as the operands of the second products.
+// are rounded to bf16 (RNE) as the operands of the second products.  Both
+// kernels run their two wave groups in ping-pong, as the forward prefill does:
+// one wave of a SIMD multiplies while its partner computes P and dS.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -303,16 +305,17 @@ __global__ __launch_bounds__(256) void bwd_prep_varlen_kernel(BwdArgs a, BwdTabl
 //   dV^T += dO^T P,  dK^T += Q^T dS         (A = dO^T / Q^T from LDS)
 // Work items t = 0, 1, ...: query tile q0 = qlast - 32 (t / 4) of query head
 // 4g + (t % 4), from the last tile qlast down to K0; a wave skips the items
-// whose rows all precede its keys.  A 3-stage LDS ring holds each item's Q
-// and dO rows and its 32 lse2 and 32 D values, loaded two items ahead.  dK^T
-// and dV^T accumulate over the items in that fixed order.
+// whose rows all precede its keys.  A 4-stage LDS ring holds each item's Q
+// and dO rows and its 32 lse2 and 32 D values, loaded two items ahead (an
+// item is read in two product phases of each wave group, see dkdv_body).
+// dK^T and dV^T accumulate over the items in that fixed order.
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 8;
 constexpr int kKvKeys = 32 * kKvWaves;
 constexpr int kQTileBytes = PermTile<32>::kBytes;     // 9 KiB
 constexpr int kKvTileLoads = PermTile<32>::kLoads;    // 9
 constexpr int kKvStageBytes = 2 * kQTileBytes + 256;  // Q, dO, lse2[32], D[32]
-constexpr int kKvStages = 3;
+constexpr int kKvStages = 4;
 // the workgroup's 256 V rows stay in LDS (a permuted padded tile) after the ring
 constexpr int kKvVBytes = PermTile<kKvKeys>::kBytes;  // 68 KiB
 constexpr int kKvVLoads = PermTile<kKvKeys>::kLoads;  // 68
@@ -356,36 +359,40 @@ __device__ __forceinline__ void kv_stage(const BwdArgs& a, const BwdSeq& sq, int
     }
 }
 
-// One work item of a wave.  Element v of an MFMA result: query
-// q0 + 8 (v >> 2) + 4h + (v & 3), key k0 + j; on an edge tile it counts when
-// k0 + j <= query < S, i.e. lo <= 8 (v >> 2) + (v & 3) < hi.  The mask is a
-// uniform branch around the selects only, so the accumulators never cross a
-// join.
-__device__ __forceinline__ void kv_item(const bf16x8 (&kf)[8], const char* sVw, const char* sQ,
-                                        const char* sD, const float* sL, int lane, int rb, int tb, float c,
-                                        bool edge, int lo, int hi, f32x16 (&acck)[4], f32x16 (&accv)[4]) {
-    const int h = lane >> 5;
-    f32x16 s = zero16(), dp = zero16();
-    // the two products side by side, the Q and dO fragments read two steps
-    // ahead of their products and the V fragments one (scheduling fences keep
-    // this order: left alone, the compiler reads every fragment first and
-    // runs out of registers)
-    bf16x8 aq[3], ad[3], bv[2];
+// One work item of a wave, in three parts (the ping-pong below runs the
+// first and last on the matrix pipe and the middle one on the vector ALU).
+// kv_first: S = Q K^T and dP = dO V^T side by side, the Q, dO and V
+// fragments read one step ahead of their products (scheduling fences keep
+// this order: left alone, the compiler reads every fragment first and runs
+// out of registers; two steps ahead spills in the ping-pong).
+__device__ __forceinline__ void kv_first(const bf16x8 (&kf)[8], const char* sVw, const char* sQ, const char* sD,
+                                         int rb, f32x16& s, f32x16& dp) {
+    s = zero16();
+    dp = zero16();
+    bf16x8 aq[2], ad[2], bv[2];
     aq[0] = row_frag(sQ, rb, 0, 0);
     ad[0] = row_frag(sD, rb, 0, 0);
     bv[0] = row_frag(sVw, rb, 0, 0);
-    aq[1] = row_frag(sQ, rb, 0, 1);
-    ad[1] = row_frag(sD, rb, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
         if (st + 1 < 8) bv[(st + 1) % 2] = row_frag(sVw, rb, 0, st + 1);
-        if (st + 2 < 8) aq[(st + 2) % 3] = row_frag(sQ, rb, 0, st + 2);
-        s = mfma(aq[st % 3], kf[st], s);
-        if (st + 2 < 8) ad[(st + 2) % 3] = row_frag(sD, rb, 0, st + 2);
-        dp = mfma(ad[st % 3], bv[st % 2], dp);
+        if (st + 1 < 8) aq[(st + 1) % 2] = row_frag(sQ, rb, 0, st + 1);
+        s = mfma(aq[st % 2], kf[st], s);
+        if (st + 1 < 8) ad[(st + 1) % 2] = row_frag(sD, rb, 0, st + 1);
+        dp = mfma(ad[st % 2], bv[st % 2], dp);
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// kv_vector: P and dS in bf16 (pb, sb).  Element v of an MFMA result: query
+// q0 + 8 (v >> 2) + 4h + (v & 3), key k0 + j; on an edge tile it counts when
+// k0 + j <= query < S, i.e. lo <= 8 (v >> 2) + (v & 3) < hi.  The mask is a
+// uniform branch around the selects only, so the accumulators never cross a
+// join.
+__device__ __forceinline__ void kv_vector(f32x16& s, f32x16& dp, const float* sL, int lane, float c, bool edge,
+                                          int lo, int hi, bf16x8 (&pb)[2], bf16x8 (&sb)[2]) {
+    const int h = lane >> 5;
 #pragma unroll
     for (int b4 = 0; b4 < 4; ++b4) {
         const float4 l2 = *reinterpret_cast<const float4*>(sL + 8 * b4 + 4 * h);
@@ -407,9 +414,16 @@ __device__ __forceinline__ void kv_item(const bf16x8 (&kf)[8], const char* sVw, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) dp[4 * b4 + i] = s[4 * b4 + i] * (dp[4 * b4 + i] - dv[i]);
     }
-    const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
-    const bf16x8 sb[2] = {pack8(dp, 0), pack8(dp, 1)};
-    // the second products, their transposed fragments read one step ahead
+    pb[0] = pack8(s, 0);
+    pb[1] = pack8(s, 1);
+    sb[0] = pack8(dp, 0);
+    sb[1] = pack8(dp, 1);
+}
+
+// kv_second: dV^T += dO^T P and dK^T += Q^T dS, the transposed fragments read
+// one step ahead.
+__device__ __forceinline__ void kv_second(const char* sQ, const char* sD, int tb, const bf16x8 (&pb)[2],
+                                          const bf16x8 (&sb)[2], f32x16 (&acck)[4], f32x16 (&accv)[4]) {
     bf16x8 td = tr_frag(sD, tb, 0, 0, 0), tq = tr_frag(sQ, tb, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -484,29 +498,74 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, const BwdSeq& sq, in
         accv[db] = zero16();
     }
     const float c = a.c;
-    for (int t = 0; t < n_items; ++t) {
-        // publish item t's stage (the item t + 1 stage may still be loading), refill
-        if (t + 1 < n_items) {
-            if (w < kKvStageLoads - (kKvLoadsMax - 1) * kKvWaves)
-                wait_vm<kKvLoadsMax>();
-            else
-                wait_vm<kKvLoadsMax - 1>();
-        } else {
-            wait_vm<0>();
+    const int grp = w >> 2;
+    // Ping-pong, as in the forward prefill: waves w and w + 4 share a SIMD;
+    // group 0 runs item t as products (the second products of item t - 1,
+    // then the first of item t) followed by the vector work of item t, group
+    // 1 the same one step behind.  One barrier per item, before the products
+    // of item t, after every wave has waited for its own loads of t; the
+    // loads of item t + 2 are issued at the start of the vector work of item
+    // t, into the stage of item t - 2 (last read in the products of t - 1).
+    // A wave skips the items whose rows all precede its keys (a suffix of
+    // the item order), but issues their loads and meets every barrier.
+    auto tile_start = [&](int t) {
+        if (t < n_items) {
+            if (t + 1 < n_items && grp == 0) {
+                if (w < kKvStageLoads - (kKvLoadsMax - 1) * kKvWaves)
+                    wait_vm<kKvLoadsMax>();
+                else
+                    wait_vm<kKvLoadsMax - 1>();
+            } else {
+                wait_vm<0>();
+            }
         }
         __syncthreads();
+    };
+    auto item_live = [&](int t) { return qlast - 32 * (t >> 2) >= k0; };
+    f32x16 s, dp;
+    bf16x8 pb[2], sb[2];
+    auto products = [&](int t) {
+        __builtin_amdgcn_s_setprio(3);
+        if (t >= 1 && item_live(t - 1)) {
+            const char* stage = smem + ((t - 1) % kKvStages) * kKvStageBytes;
+            kv_second(stage, stage + kQTileBytes, tb, pb, sb, acck, accv);
+        }
+        if (t < n_items && item_live(t)) {
+            const char* stage = smem + (t % kKvStages) * kKvStageBytes;
+            kv_first(kf, sV + 32 * w * kRowBytes, stage, stage + kQTileBytes, rb, s, dp);
+        }
+    };
+    auto vector_work = [&](int t) {
+        __builtin_amdgcn_s_setprio(0);
         if (t + 2 < n_items)
             kv_stage(a, sq, g, t + 2, qlast, plan, smem + ((t + 2) % kKvStages) * kKvStageBytes, w, lane);
-
-        const int64_t q0 = qlast - 32 * (t >> 2);
-        if (q0 < k0) continue;  // every key of this wave lies after every row of the tile
-        const char* stage = smem + (t % kKvStages) * kKvStageBytes;
-        const bool edge = q0 == k0 || q0 + 32 > S;
-        const int lo = (int)(k0 - q0) + j - 4 * h;
-        const int hi = (int)(S - q0 < 64 ? S - q0 : 64) - 4 * h;
-        kv_item(kf, sV + 32 * w * kRowBytes, stage, stage + kQTileBytes,
-                reinterpret_cast<const float*>(stage + 2 * kQTileBytes), lane, rb, tb, c, edge, lo, hi, acck, accv);
+        if (item_live(t)) {
+            const int64_t q0 = qlast - 32 * (t >> 2);
+            const char* stage = smem + (t % kKvStages) * kKvStageBytes;
+            const bool edge = q0 == k0 || q0 + 32 > S;
+            const int lo = (int)(k0 - q0) + j - 4 * h;
+            const int hi = (int)(S - q0 < 64 ? S - q0 : 64) - 4 * h;
+            kv_vector(s, dp, reinterpret_cast<const float*>(stage + 2 * kQTileBytes), lane, c, edge, lo, hi, pb, sb);
+        }
+    };
+    if (grp == 0) {
+        for (int t = 0; t < n_items; ++t) {
+            tile_start(t);
+            products(t);
+            vector_work(t);
+        }
+        tile_start(n_items);
+        products(n_items);
+    } else {
+        tile_start(0);
+        products(0);
+        for (int t = 0; t < n_items; ++t) {
+            tile_start(t + 1);
+            vector_work(t);
+            products(t + 1);
+        }
     }
+    __builtin_amdgcn_s_setprio(0);
     const int64_t row = (kv0 + k0 + j) * kHeadDim;
     if (k0 + j < S) {
         store_col(a.dv + row, accv, 1.0f, h);
@@ -548,11 +607,11 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_varlen_kernel(BwdArgs 
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 8 waves = the 4 query heads of one KV head x 2 halves of
 // the 64 positions [64 pb, 64 pb + 64), as in the forward; K / V tiles of 64
-// keys (K and V, permuted padded tiles) stream through a 3-stage ring, loads two
+// keys (K and V, permuted padded tiles) stream through a 4-stage ring, loads two
 // tiles ahead.  Wave column j is query row 64 pb + 32 (w >> 2) + j.
 // ---------------------------------------------------------------------------
 constexpr int kDqWaves = 8;
-constexpr int kDqStages = 3;
+constexpr int kDqStages = 4;
 constexpr int kDqTileLoads = PermTile<64>::kLoads;  // 17
 constexpr int kDqTileBytes = PermTile<64>::kBytes;  // 17 KiB
 constexpr int kDqStageBytes = 2 * kDqTileBytes;     // K, V
@@ -637,29 +696,53 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = zero16();
     const float c = a.c;
+    const int grp = w >> 2;
+    const int T = t_last;
 
-    for (int t = 0; t <= t_last; ++t) {
-        if (t + 1 <= t_last) {
-            if (w < kDqStageLoads - (kDqLoadsMax - 1) * kDqWaves)
-                wait_vm<kDqLoadsMax>();
-            else
-                wait_vm<kDqLoadsMax - 1>();
-        } else {
-            wait_vm<0>();
+    // Ping-pong, as in the forward prefill: waves w and w + 4 share a SIMD;
+    // group 0 runs tile t as products (dQ of tile t - 1, then S and dP of
+    // tile t) followed by the vector work of tile t (P, dS), group 1 the same
+    // one step behind.  One barrier per tile, before the products of tile t,
+    // after every wave has waited for its own loads of t; the loads of tile
+    // t + 2 are issued at the start of the vector work of tile t, into the
+    // stage of tile t - 2 (last read, as K^T, in the products of t - 1).
+    auto tile_start = [&](int t) {
+        if (t <= T) {
+            if (t + 1 <= T && grp == 0) {
+                if (w < kDqStageLoads - (kDqLoadsMax - 1) * kDqWaves)
+                    wait_vm<kDqLoadsMax>();
+                else
+                    wait_vm<kDqLoadsMax - 1>();
+            } else {
+                wait_vm<0>();
+            }
         }
         __syncthreads();
-        if (t + 2 <= t_last) {
-            char* nb = smem + ((t + 2) % kDqStages) * kDqStageBytes;
-            dq_stage(kbase, vbase, (int64_t)(t + 2) * kTile, S, plan, nb, w);
+    };
+    f32x16 s[2], dp[2];
+    bf16x8 sb[4];
+    auto products = [&](int t) {
+        __builtin_amdgcn_s_setprio(3);
+        if (t >= 1) {
+            // dQ^T += K^T dS^T of tile t - 1, the transposed K fragments read two steps ahead
+            const char* sK = smem + ((t - 1) % kDqStages) * kDqStageBytes;
+            bf16x8 ft[3];
+            ft[0] = tr_frag(sK, tb, 0, 0, 0);
+            ft[1] = tr_frag(sK, tb, 0, 0, 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const int ku = x >> 2, db = x & 3;  // ku = 2 kb + u
+                if (x + 2 < 16) ft[(x + 2) % 3] = tr_frag(sK, tb, (x + 2) >> 3, ((x + 2) >> 2) & 1, (x + 2) & 3);
+                acc[db] = mfma(ft[x % 3], sb[ku], acc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        const char* sK = smem + (t % kDqStages) * kDqStageBytes;
-        const char* sV = sK + kDqTileBytes;
-        const int64_t key0 = (int64_t)t * kTile;
-
-        f32x16 s[2], dp[2];
-        {
-            // the 32 products of S^T and dP^T, each pair's K and V fragments
-            // read two steps ahead (scheduling fences keep this order)
+        if (t <= T) {
+            // the 32 products of S^T and dP^T of tile t, each pair's K and V
+            // fragments read two steps ahead (scheduling fences keep this order)
+            const char* sK = smem + (t % kDqStages) * kDqStageBytes;
+            const char* sV = sK + kDqTileBytes;
             s[0] = zero16();
             dp[0] = zero16();
             s[1] = zero16();
@@ -680,6 +763,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+    // P and dS of tile t (bf16 in sb), after issuing this wave's loads of tile t + 2
+    auto vector_work = [&](int t) {
+        __builtin_amdgcn_s_setprio(0);
+        if (t + 2 <= T) dq_stage(kbase, vbase, (int64_t)(t + 2) * kTile, S, plan,
+                                 smem + ((t + 2) % kDqStages) * kDqStageBytes, w);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -688,8 +777,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
         // diagonal tile only (a uniform branch around the selects): element v
         // of block kb is key key0 + 32 kb + 8 (v >> 2) + 4h + (v & 3), visible
         // when that is <= pos, i.e. 32 kb + 8 (v >> 2) + (v & 3) <= vis
-        if (t == t_last) {
-            const int vis = (int)(pos - key0) - 4 * h;  // pos - key0 in [0, 63]
+        if (t == T) {
+            const int vis = (int)(pos - (int64_t)t * kTile) - 4 * h;  // pos - key0 in [0, 63]
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -701,22 +790,29 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, const BwdSeq& sq, int 
 #pragma unroll
             for (int v = 0; v < 16; ++v) dp[kb][v] = s[kb][v] * (dp[kb][v] - Di);
         }
-        {
-            // dQ^T += K^T dS^T, the transposed K fragments read two steps ahead
-            const bf16x8 sb[4] = {pack8(dp[0], 0), pack8(dp[0], 1), pack8(dp[1], 0), pack8(dp[1], 1)};
-            bf16x8 ft[3];
-            ft[0] = tr_frag(sK, tb, 0, 0, 0);
-            ft[1] = tr_frag(sK, tb, 0, 0, 1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const int ku = x >> 2, db = x & 3;  // ku = 2 kb + u
-                if (x + 2 < 16) ft[(x + 2) % 3] = tr_frag(sK, tb, (x + 2) >> 3, ((x + 2) >> 2) & 1, (x + 2) & 3);
-                acc[db] = mfma(ft[x % 3], sb[ku], acc[db]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        sb[0] = pack8(dp[0], 0);
+        sb[1] = pack8(dp[0], 1);
+        sb[2] = pack8(dp[1], 0);
+        sb[3] = pack8(dp[1], 1);
+    };
+    if (grp == 0) {
+        for (int t = 0; t <= T; ++t) {
+            tile_start(t);
+            products(t);
+            vector_work(t);
+        }
+        tile_start(T + 1);
+        products(T + 1);
+    } else {
+        tile_start(0);
+        products(0);
+        for (int t = 0; t <= T; ++t) {
+            tile_start(t + 1);
+            vector_work(t);
+            products(t + 1);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 
     if (active) store_col(a.dq + (qrow0 + pos) * kHeadDim, acc, a.scale, h);
 }
