@@ -357,6 +357,32 @@ def backward_section(kb, torch, dev, qd, kd, vd, out_pre, reps: int, check: bool
     return res
 
 
+DATA_STUDY_CASES = ("bench inputs", "V = 0", "Q = 0", "Q = K = V = 0")
+
+
+def data_study(kb, torch, qd, kd, vd, reps: int) -> list:
+    """The prefill on the bench shape, `reps` launches on each case of
+    DATA_STUDY_CASES in that order; median launch time of each (HIP events)."""
+    z = torch.zeros_like
+    cases = {"bench inputs": (qd, kd, vd), "V = 0": (qd, kd, z(vd)), "Q = 0": (z(qd), kd, vd),
+             "Q = K = V = 0": (z(qd), z(kd), z(vd))}
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    res = []
+    for name in DATA_STUDY_CASES:
+        qx, kx, vx = cases[name]
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            kb.prefill(qx, kx, vx, out=out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res.append({"case": name, "ms_median": float(np.median(ts)), "launches": reps})
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +396,9 @@ def main() -> int:
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--backward-only", type=int, default=0, metavar="N",
                     help="only run prefill_lse once and the backward N times (profiling runs of the backward)")
+    ap.add_argument("--data-study", type=int, default=0, metavar="N",
+                    help="only run the prefill N times on each of four inputs of the bench shape (the bench's, "
+                         "V = 0, Q = 0, Q = K = V = 0): same instructions and traffic, different operand switching")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this operator is built and measured per GPU "
@@ -401,6 +430,9 @@ def main() -> int:
     if args.backward_only:
         bwd = backward_section(kb, torch, dev, qd, kd, vd, None, reps=args.backward_only, check=False)
         print(json.dumps({"backward": bwd}))
+        return 0
+    if args.data_study:
+        print(json.dumps({"data_study": data_study(kb, torch, qd, kd, vd, args.data_study)}))
         return 0
     q_chunks = [qd[:, :, c * PART:(c + 1) * PART].contiguous() for c in range(S // PART)]
     q_dec = qd[:, :, DEC_LEN - 1:DEC_LEN].contiguous()

@@ -10,7 +10,9 @@ The GPU runs (each command runs committed files only):
       (three passes, SQ_PASSES below; the third reads the GPU's active cycles, so that
       cycles / dispatch time gives the clock the kernel ran at)
   and for the backward kernels, the same --kernel-trace --stats, FETCH_SIZE and
-  WRITE_SIZE runs of `python3 bench.py --backward-only 3`.
+  WRITE_SIZE runs of `python3 bench.py --backward-only 3`; and, for the
+  prefill's clock against its input data,
+  rocprofv3 --pmc GRBM_GUI_ACTIVE GRBM_COUNT -d <data> -o run --output-format csv -- python3 bench.py --data-study 7
 Then, on any host:
   python bench_profile.py --stats <stats> --fetch <fetch> --write <write> \
       --copy-fetch <copy_fetch> --copy-write <copy_write> [--sq <sq1> <sq2>] \
@@ -244,6 +246,37 @@ def write_summaries(kernels, stats, fetch, write, f_fetch, f_write, src_hash, ou
         print(f"{k}: avg {avg_us:.1f} us, HBM {hbm:.3e} B/launch")
 
 
+def data_study_summary(d: str, out: str, src_hash: str, reps: int = 7) -> None:
+    """Per-case duration and clock of the prefill launches of bench.py
+    --data-study (cases in bench.DATA_STUDY_CASES order, `reps` each)."""
+    rows = {}
+    for r in csv.DictReader(open(find_csv(d, "counter_collection.csv"))):
+        if short(r["Kernel_Name"]) != "prefill_kernel<false>":
+            continue
+        x = rows.setdefault(int(r["Dispatch_Id"]), {})
+        x[r["Counter_Name"]] = float(r["Counter_Value"])
+        x["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    disp = [rows[k] for k in sorted(rows)]
+    assert len(disp) == reps * len(bench.DATA_STUDY_CASES), len(disp)
+    lines = ["# prefill_kernel<false>: clock and duration by input data, B=16 S=16384 (same instructions and traffic)",
+             f"kernel hash (code without comments, and compiler flags): {src_hash}", "",
+             "command:",
+             f"  rocprofv3 --pmc GRBM_GUI_ACTIVE GRBM_COUNT -d <data> -o run --output-format csv -- python3 bench.py "
+             f"--data-study {reps}",
+             "  python bench_profile.py ... --data-study <data> --out profiles", "",
+             "per case, median over its launches but the first (clock = GRBM_COUNT / (8 XCDs x duration)):"]
+    for i, name in enumerate(bench.DATA_STUDY_CASES):
+        sel = disp[i * reps + 1:(i + 1) * reps]
+        ms = statistics.median(x["ns"] for x in sel) * 1e-6
+        ghz = statistics.median(x["GRBM_COUNT"] / 8 / x["ns"] for x in sel)
+        lines.append(f"  {name:16s} {ms:8.3f} ms  {ghz:5.3f} GHz  time x clock {ms * ghz:6.1f} million cycles  "
+                     f"({bench.prefill_flops(bench.B, 0, bench.S) / (ms * 1e-3) / 2.5e15:.3f} of the 2.5 PFLOP/s peak)")
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "prefill_kernel_b16_s16384_clock_by_data.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines[-len(bench.DATA_STUDY_CASES):]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     for a in ("stats", "fetch", "write", "copy_fetch", "copy_write", "out"):
@@ -254,7 +287,11 @@ def main():
     for a in ("bwd_stats", "bwd_fetch", "bwd_write"):
         ap.add_argument("--" + a.replace("_", "-"), default=None,
                         help="rocprofv3 output of bench.py --backward-only 3 (stats, FETCH_SIZE, WRITE_SIZE)")
+    ap.add_argument("--data-study", default=None,
+                    help="rocprofv3 GRBM counter run of bench.py --data-study N (the prefill's clock by input data)")
     args = ap.parse_args()
+    if args.data_study:
+        data_study_summary(args.data_study, args.out, bench.kernel_source_hash())
     f_fetch, f_write = copy_factor(args.copy_fetch), copy_factor(args.copy_write)
     stats = {}
     for r in csv.DictReader(open(find_csv(args.stats, "kernel_stats.csv"))):
