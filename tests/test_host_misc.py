@@ -181,3 +181,33 @@ def test_binding_accepts_matching_output(cpu_binding, monkeypatch):
     out = _bf(1, 4, 64, 128)
     assert kb.prefill(q, k, v, out=out) is out
     assert fake.calls == ["kb_attn_prefill"]
+
+
+def test_data_study_summary_reads_clock_per_case(tmp_path):
+    """bench_profile's clock-by-input summary: per case (launches in
+    bench.DATA_STUDY_CASES order, the first of each dropped), the median
+    duration and GRBM_COUNT / (8 XCDs x duration)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import bench_profile
+
+    reps = 3
+    src = tmp_path / "data" / "run_counter_collection.csv"
+    src.parent.mkdir()
+    lines = ["Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp"]
+    d = 0
+    for i, _ in enumerate(bench.DATA_STUDY_CASES):
+        ghz = 1.5 + 0.25 * i
+        for r in range(reps):
+            d += 1
+            ns = 20_000_000 + 1_000_000 * i + (5_000_000 if r == 0 else 0)  # the first launch is slower
+            lines.append(f"{d},prefill_kernel<false>(kb::PrefillArgs),1,GRBM_COUNT,{8 * ghz * ns},0,{ns}")
+            lines.append(f"{d},prefill_kernel<false>(kb::PrefillArgs),1,GRBM_GUI_ACTIVE,{8 * ghz * ns},0,{ns}")
+        d += 1
+        lines.append(f"{d},decode_kernel(kb::DecodeArgs),1,GRBM_COUNT,1,0,1")
+    src.write_text("\n".join(lines) + "\n")
+    bench_profile.data_study_summary(str(tmp_path / "data"), str(tmp_path / "out"), "h", reps=reps)
+    text = (tmp_path / "out" / "prefill_kernel_b16_s16384_clock_by_data.txt").read_text()
+    for i, name in enumerate(bench.DATA_STUDY_CASES):
+        line = next(l for l in text.splitlines() if l.strip().startswith(name + " "))
+        assert f"{20 + i:.3f} ms" in line and f"{1.5 + 0.25 * i:.3f} GHz" in line, line
