@@ -234,21 +234,37 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
     close_chunk();
     __builtin_amdgcn_s_setprio(0);
 
-    if (active) {
-        uint16_t* orow = wk.o0 + (qrow0 + r) * kHeadDim;
+    // The quotients of this lane's row, 4 columns per 8-byte piece: piece
+    // (db, b4) holds columns 32 db + 8 b4 + 4 h .. + 3.  Swapping halves of
+    // the wave between the pieces of b4 = 2m and 2m + 1 gives every lane the
+    // 8 adjacent columns 32 db + 16 m + 8 h .. + 7, one 16-byte store.  The
+    // swaps run in every lane (they read the partner lane), the stores only
+    // in the active ones.
+    {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
-            for (int b4 = 0; b4 < 4; ++b4) {
-                const uint32_t e0 = finalize(O[db][4 * b4 + 0], L), e1 = finalize(O[db][4 * b4 + 1], L);
-                const uint32_t e2 = finalize(O[db][4 * b4 + 2], L), e3 = finalize(O[db][4 * b4 + 3], L);
-                uint2 packed;
-                packed.x = e0 | (e1 << 16);
-                packed.y = e2 | (e3 << 16);
-                *reinterpret_cast<uint2*>(orow + 32 * db + 8 * b4 + 4 * h) = packed;
+            for (int m = 0; m < 2; ++m) {
+                uint32_t a[2], b[2];
+#pragma unroll
+                for (int hv = 0; hv < 2; ++hv) {
+                    const int va = 4 * (2 * m) + 2 * hv, vb = 4 * (2 * m + 1) + 2 * hv;
+                    a[hv] = finalize(O[db][va], L) | ((uint32_t)finalize(O[db][va + 1], L) << 16);
+                    b[hv] = finalize(O[db][vb], L) | ((uint32_t)finalize(O[db][vb + 1], L) << 16);
+                }
+                u32x4 out;
+#pragma unroll
+                for (int hv = 0; hv < 2; ++hv) {
+                    // new first operand: lanes 32..63 take b of lanes 0..31;
+                    // new second: lanes 0..31 take a of lanes 32..63
+                    const auto sw = __builtin_amdgcn_permlane32_swap(a[hv], b[hv], false, false);
+                    out[hv] = (uint32_t)sw[0];
+                    out[2 + hv] = (uint32_t)sw[1];
+                }
+                if (active) *reinterpret_cast<u32x4*>(wk.o0 + (qrow0 + r) * kHeadDim + 32 * db + 16 * m + 8 * h) = out;
             }
         }
-        if (wk.lse0 && h == 0) wk.lse0[qrow0 + r] = lse_of(Mc, L);
+        if (active && wk.lse0 && h == 0) wk.lse0[qrow0 + r] = lse_of(Mc, L);
     }
 }
 
