@@ -5,7 +5,7 @@ One step is one pass of the whole path over one batch of synthetic input
 channels x8, V ~ N(0,1), scale 1/sqrt(128)):
   1. full causal prefill of the 16384 rows              (prefill_kernel<false>)
   2. partitioned forward of the same rows in 16 chunks of 1024 against the
-     cached K/V                                           (prefill_kernel<true>)
+     cached K/V (2048 blocks per call, 8 per CU)     (prefill_persistent_kernel<true>)
   3. one-token decode at context 8192 (split-KV chunks + in-order combine)
 Inputs are resident in HBM before the timed region.  Outside the step the
 line also reports a decode sweep, a ragged batch, a paged-cache decode, a

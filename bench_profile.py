@@ -44,8 +44,9 @@ STATS_ARGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-extras"
 STATS_WARMUP_STEPS = 2
 KERNELS = {
     "prefill_kernel<false>": ("prefill_kernel_b16_s16384", "full causal prefill B=16 S=16384 (one launch per step)"),
-    "prefill_kernel<true>": ("prefill_kernel_partitioned_b16_16x1024",
-                             "partitioned forward, 16 launches of 1024 rows against the S=16384 cache"),
+    "prefill_persistent_kernel<true>": ("prefill_kernel_partitioned_b16_16x1024",
+                                        "partitioned forward, 16 launches of 1024 rows against the S=16384 cache "
+                                        "(2048 blocks per launch, 8 per CU: the persistent kernel)"),
     "decode_kernel": ("decode_kernel_b16_l8192", "decode split-KV at context 8192, B=16 (8 chunks)"),
     "combine_kernel": ("combine_kernel_b16_l8192", "decode combine of 8 chunks, B=16"),
 }
@@ -303,7 +304,8 @@ def main():
     write_summaries(KERNELS, stats, per_dispatch(args.fetch), per_dispatch(args.write), f_fetch, f_write, src_hash,
                     args.out, STATS_ARGS, "--steps 1 --warmup 0 --no-cpu-baseline --no-extras",
                     {"prefill_kernel<false>": bench.prefill_flops(bench.B, 0, bench.S),
-                     "prefill_kernel<true>": bench.prefill_flops(bench.B, 0, bench.S) // (bench.S // bench.PART)},
+                     "prefill_persistent_kernel<true>":
+                         bench.prefill_flops(bench.B, 0, bench.S) // (bench.S // bench.PART)},
                     trace_durations(args.stats, KERNELS), STATS_WARMUP_STEPS, 5)
     if args.bwd_stats:
         bstats = {}

@@ -2,7 +2,10 @@
 //
 // Three kernels, all built on the contract in kb_contract.h:
 //   prefill_kernel  full-sequence prefill and partitioned forward (the same
-//                   kernel: row r sits at position kv_len - q_len + r)
+//                   kernel: row r sits at position kv_len - q_len + r); one
+//                   workgroup per 64-position block, or, for launches of 2 to
+//                   16 blocks per CU, prefill_persistent_kernel: one
+//                   workgroup per CU walking a fixed list of blocks
 //   decode_kernel   one query token; the 4 query heads of a KV head share
 //                   one MFMA tile (columns 0..3); one workgroup per
 //                   (batch, KV head, chunk of 1024 keys)
@@ -268,18 +271,17 @@ __device__ __forceinline__ void prefill_body(const PrefillWork& wk, float c, cha
     }
 }
 
-// Dense batch: q, o [batch, Hq, q_len, 128]; k, v [batch, Hkv, cap, 128].
-template <bool kPartitioned>
-__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kStages * PaddedTile::kBytes];
+// Work item x of a dense-batch launch (A: the launch's PrefillArgs, read
+// from wherever the caller holds them).  Workgroups are dispatched to the 8
+// XCDs round-robin (x % 8); when the (b, g) pairs split evenly over the
+// XCDs, XCD k takes the pairs k, k + 8, ... one after another, each pair's
+// position blocks longest first, so the blocks running together on an XCD
+// stream the same K/V tiles through its L2.
+template <class A>
+__device__ __forceinline__ void prefill_item(const A& a, int x, PrefillWork& wk) {
     const int nbg = a.batch * a.n_kv_heads;
-    const int x = blockIdx.x;
     int bg, pbr;
     if ((nbg & 7) == 0) {
-        // workgroups are dispatched to the 8 XCDs round-robin (x % 8); give XCD
-        // k the (b, g) pairs k, k + 8, ... one after another, each pair's
-        // position blocks longest first, so the blocks running together on an
-        // XCD stream the same K/V tiles through its L2
         const int i = x >> 3;
         bg = (i / a.n_pb) * 8 + (x & 7);
         pbr = i % a.n_pb;
@@ -289,7 +291,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
     }
     const int b = bg / a.n_kv_heads, g = bg % a.n_kv_heads;
     const int n_q_heads = kGroup * a.n_kv_heads;
-    PrefillWork wk;
     wk.q0 = a.q + ((int64_t)b * n_q_heads + kGroup * g) * a.q_len * kHeadDim;
     wk.o0 = a.o + ((int64_t)b * n_q_heads + kGroup * g) * a.q_len * kHeadDim;
     wk.lse0 = a.lse ? a.lse + ((int64_t)b * n_q_heads + kGroup * g) * a.q_len : nullptr;
@@ -300,7 +301,45 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs
     wk.q_len = a.q_len;
     wk.kv_len = a.kv_len;
     wk.pb = a.pb_first + a.n_pb - 1 - pbr;
+}
+
+// Dense batch: q, o [batch, Hq, q_len, 128]; k, v [batch, Hkv, cap, 128].
+// One workgroup per work item.
+template <bool kPartitioned>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * PaddedTile::kBytes];
+    PrefillWork wk;
+    prefill_item(a, blockIdx.x, wk);
     prefill_body<kPartitioned>(wk, a.c, smem);
+}
+
+// The same work items, run by 8 U resident workgroups (one per CU: the LDS
+// ring fills a CU) that each walk a fixed list, which saves the launch of a
+// workgroup per item where items are few per CU.  Workgroup p sits on XCD
+// k = p % 8 with local index u = p / 8 and takes XCD k's items x = 8 i + k
+// in rounds of U: in round n, i = n U + u for even n and n U + U - 1 - u for
+// odd n, so that two consecutive rounds give every workgroup the same number
+// of tiles when the launch admits it (the launcher checks).  A barrier
+// between items keeps the next item's first loads from reaching ring stages
+// that the slower wave group still reads.  The arguments are read from the
+// kernel-argument segment (PrefillArgs is the first argument, at offset 0)
+// at each item, through a pointer the compiler cannot see as invariant, so
+// that they hold no scalar registers across an item's tiles.
+template <bool kPartitioned>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_persistent_kernel(PrefillArgs a, int n_items) {
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * PaddedTile::kBytes];
+    const int k = blockIdx.x & 7, u = blockIdx.x >> 3, U = gridDim.x >> 3;
+    const int n_k = (n_items - k + 7) >> 3;  // items x < n_items with x % 8 == k
+    for (int n = 0;; ++n) {
+        const int i = n * U + ((n & 1) ? U - 1 - u : u);
+        if (i >= n_k) break;
+        uint64_t args = (uint64_t)(uintptr_t)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(args));
+        PrefillWork wk;
+        prefill_item(*reinterpret_cast<const __attribute__((address_space(4))) PrefillArgs*>(args), 8 * i + k, wk);
+        if (n > 0) __syncthreads();
+        prefill_body<kPartitioned>(wk, a.c, smem);
+    }
 }
 
 // Ragged batch: the sequences of one launch (at most kMaxVarlenSeqs), packed
@@ -818,6 +857,43 @@ int static_scratch(void** out) {
     return KB_ATTN_OK;
 }
 
+// CUs of the current device when their number is a multiple of the 8 XCDs,
+// else 0; looked up once per device and kept.
+int resident_prefill_workgroups() {
+    static std::mutex mu;
+    static int cus[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            n = 0;
+        }
+        cus[dev] = (n > 0 && n % 8 == 0) ? n : -1;
+    }
+    return cus[dev] > 0 ? cus[dev] : 0;
+}
+
+// The persistent prefill runs when its fixed schedule balances and pays: the
+// (b, g) pairs split evenly over the XCDs, each XCD's item count is a whole
+// number of round pairs, and a pair's position blocks either fill whole
+// round pairs or divide a round (then every two consecutive rounds give each
+// workgroup the same tiles); and there are 2 to 16 items per workgroup (with
+// more, the launch cost it saves is a smaller share than the balance the
+// hardware's own dispatch keeps: measured slower at 128 per workgroup).
+bool use_persistent_prefill(const PrefillArgs& a, int64_t n_items, int resident) {
+    if (resident <= 0) return false;
+    const int64_t U = resident / 8, nbg = (int64_t)a.batch * a.n_kv_heads;
+    if (nbg % 8 != 0 || n_items < 2 * (int64_t)resident || n_items > 16 * (int64_t)resident) return false;
+    if ((n_items / 8) % (2 * U) != 0) return false;
+    return a.n_pb % (2 * U) == 0 || U % a.n_pb == 0;
+}
+
 int launch_prefill(bool partitioned, const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t batch, int64_t q_len, int64_t kv_len, int64_t cap, int32_t n_kv_heads, float scale,
                    hipStream_t stream) {
@@ -838,10 +914,19 @@ int launch_prefill(bool partitioned, const void* q, const void* k, const void* v
     a.c = contract_c(scale);
     const int64_t grid = (int64_t)a.n_pb * batch * n_kv_heads;
     if (grid > INT32_MAX) return KB_ATTN_ERR_LENGTH;
-    if (!partitioned)
+    const int resident = resident_prefill_workgroups();
+    if (use_persistent_prefill(a, grid, resident)) {
+        if (!partitioned)
+            hipLaunchKernelGGL(prefill_persistent_kernel<false>, dim3((unsigned)resident), dim3(64 * kPrefillWaves), 0,
+                               stream, a, (int)grid);
+        else
+            hipLaunchKernelGGL(prefill_persistent_kernel<true>, dim3((unsigned)resident), dim3(64 * kPrefillWaves), 0,
+                               stream, a, (int)grid);
+    } else if (!partitioned) {
         hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(64 * kPrefillWaves), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(64 * kPrefillWaves), 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? KB_ATTN_OK : KB_ATTN_ERR_HIP;
 }
 
