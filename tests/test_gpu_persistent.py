@@ -69,3 +69,24 @@ def test_persistent_partitioned_equals_one_block_launches(kb):
     flat = (rows // q_len) * S + r0 + rows % q_len
     ref = oracle.attention(q, k, v, rows=flat, threads=oracle_threads())
     compare(part.reshape(-1, D)[rows], ref, f"persistent partitioned B={B} sampled rows")
+
+
+def test_persistent_partitioned_rows_off_the_block_grid(kb):
+    # B=8, 1000 rows at positions 15384..16383: the first 64-position block
+    # (15360..15423) holds 24 positions before the first row, so its lanes
+    # for them store nothing; 8 * 8 * 16 = 1024 blocks, 4 per CU
+    B, S, seed, q_len = 8, 16384, 13, 1000
+    q, k, v = kb_gen.attention_inputs(seed, B, S)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    r0 = S - q_len
+    note(f"persistent partitioned B={B} rows {r0}..{S - 1} kv_len {S}")
+    out = kb.partitioned(qd[:, :, r0:].contiguous(), kd, vd, kv_len=S)
+    part = bits(out)
+    for a, n in ((0, 40), (40, 128), (872, 128)):
+        note(f"partitioned rows {r0 + a}..{r0 + a + n - 1} (one workgroup per block)")
+        small = kb.partitioned(qd[:, :, r0 + a:r0 + a + n].contiguous(), kd, vd, kv_len=r0 + a + n)
+        same_bits(bits(small), part[:, :, a:a + n], f"rows {r0 + a}..{r0 + a + n - 1}")
+    rows = sample_rows(np.random.default_rng(seed), B, HQ, q_len, extra=2, fixed=(0, 1, 23, 24, 25, 39, 40, 999))
+    flat = (rows // q_len) * S + r0 + rows % q_len
+    ref = oracle.attention(q, k, v, rows=flat, threads=oracle_threads())
+    compare(part.reshape(-1, D)[rows], ref, f"persistent partitioned B={B} q_len={q_len} sampled rows")

@@ -54,9 +54,9 @@ def schedule(n_items, resident):
 
 
 # (batch, q_len, kv_len): the pages' B=1 set, B=4 S=4096, 1024- and
-# 2048-row partitioned calls, the two test shapes of test_gpu_persistent.py
+# 2048-row partitioned calls, the test shapes of test_gpu_persistent.py
 ADMITTED = [(1, 4096, 4096), (1, 8192, 8192), (1, 16384, 16384), (4, 4096, 4096), (2, 8192, 8192),
-            (8, 1024, 2048), (8, 1024, 8192), (16, 1024, 16384), (4, 2048, 8192)]
+            (8, 1024, 2048), (8, 1024, 8192), (16, 1024, 16384), (4, 2048, 8192), (8, 1000, 16384)]
 REFUSED = [(1, 1024, 1024), (8, 8192, 8192), (16, 16384, 16384), (3, 5000, 5000), (1, 4000, 4000),
            (2, 100, 9000), (1, 1000, 4096)]
 
