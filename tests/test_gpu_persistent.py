@@ -90,3 +90,19 @@ def test_persistent_partitioned_rows_off_the_block_grid(kb):
     flat = (rows // q_len) * S + r0 + rows % q_len
     ref = oracle.attention(q, k, v, rows=flat, threads=oracle_threads())
     compare(part.reshape(-1, D)[rows], ref, f"persistent partitioned B={B} q_len={q_len} sampled rows")
+
+
+def test_persistent_prefill_two_blocks_per_cu(kb):
+    # B=1 S=4096: 8 * 64 = 512 blocks, 2 per CU (one even round, one odd)
+    B, S, seed = 1, 4096, 14
+    q, k, v = kb_gen.attention_inputs(seed, B, S)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    note(f"persistent prefill B={B} S={S} seed={seed}")
+    pre = bits(kb.prefill(qd, kd, vd))
+    for r0 in (0, 1984, 3968):
+        note(f"partitioned rows {r0}..{r0 + 127} at kv_len {r0 + 128} (one workgroup per block)")
+        part = kb.partitioned(qd[:, :, r0:r0 + 128].contiguous(), kd, vd, kv_len=r0 + 128)
+        same_bits(bits(part), pre[:, :, r0:r0 + 128], f"prefill rows {r0}..{r0 + 127}")
+    rows = sample_rows(np.random.default_rng(seed), B, HQ, S, extra=8)
+    compare(pre.reshape(-1, D)[rows], oracle.attention(q, k, v, rows=rows, threads=oracle_threads()),
+            f"persistent prefill B={B} S={S} sampled rows")
