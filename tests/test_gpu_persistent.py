@@ -106,3 +106,19 @@ def test_persistent_prefill_two_blocks_per_cu(kb):
     rows = sample_rows(np.random.default_rng(seed), B, HQ, S, extra=8)
     compare(pre.reshape(-1, D)[rows], oracle.attention(q, k, v, rows=rows, threads=oracle_threads()),
             f"persistent prefill B={B} S={S} sampled rows")
+
+
+def test_persistent_prefill_lse_equals_one_block_launches(kb):
+    # the log-sum-exp output of the persistent path (B=2 S=8192, 8 blocks per
+    # CU) against one-workgroup-per-block partitioned_lse calls, bit for bit
+    B, S, seed = 2, 8192, 15
+    q, k, v = kb_gen.attention_inputs(seed, B, S)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    note(f"persistent prefill_lse B={B} S={S} seed={seed}")
+    o, lse = kb.prefill_lse(qd, kd, vd)
+    o_bits, lse_bits = bits(o), lse.cpu().numpy().view(np.uint32)
+    for r0 in (0, 2048, 8064):
+        note(f"partitioned_lse rows {r0}..{r0 + 127} (one workgroup per block)")
+        oc, lc = kb.partitioned_lse(qd[:, :, r0:r0 + 128].contiguous(), kd, vd, r0 + 128)
+        same_bits(bits(oc), o_bits[:, :, r0:r0 + 128], f"o rows {r0}..{r0 + 127}")
+        same_bits(lc.cpu().numpy().view(np.uint32), lse_bits[:, :, r0:r0 + 128], f"lse rows {r0}..{r0 + 127}")
