@@ -657,13 +657,12 @@ struct CombineArgs {
 __device__ __forceinline__ void combine_row(const float* ws_o, const float* ws_ml, int64_t base, int n_chunks,
                                             uint16_t* orow, float* lse_row) {
     const int d = threadIdx.x;
-    float Mc = ws_ml[base * 2 + 0];
-    float L = ws_ml[base * 2 + 1];
-    float O = ws_o[base * kHeadDim + d];
-    // partials are loaded kBatch chunks at a time, then folded one by one in
-    // chunk order, so the loads of a batch are in flight together
+    // partials are loaded kBatch chunks at a time (chunk 0 with the first
+    // batch), then folded one by one in chunk order, so the loads of a batch
+    // are in flight together; chunk 0 is the total the others fold into
     constexpr int kBatch = 8;
-    for (int k0 = 1; k0 < n_chunks; k0 += kBatch) {
+    float Mc = 0.0f, L = 0.0f, O = 0.0f;
+    for (int k0 = 0; k0 < n_chunks; k0 += kBatch) {
         float mcs[kBatch], ls[kBatch], os[kBatch];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
@@ -674,7 +673,11 @@ __device__ __forceinline__ void combine_row(const float* ws_o, const float* ws_m
         }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
-            if (k0 + i < n_chunks) {
+            if (k0 + i == 0) {
+                Mc = mcs[0];
+                L = ls[0];
+                O = os[0];
+            } else if (k0 + i < n_chunks) {
                 float Mcn, A, B;
                 fold_scalars(Mc, mcs[i], Mcn, A, B);
                 L = __builtin_fmaf(L, A, ls[i] * B);
