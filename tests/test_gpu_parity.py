@@ -116,6 +116,13 @@ def test_prefill_b16_s16384_outliers_and_decode_8192(kb):
     note("decode kv_len=8192 over the S=16384 cache")
     dec = kb.decode(qd[:, :, 8191:8192].contiguous(), kd, vd, kv_len=8192)
     assert_same_bits(bits(dec)[:, :, 0], bits(pre[:, :, 8191]), "decode(8192) vs prefill row 8191")
+    # the bench's partitioned calls (1024 rows against the cache; 2048 blocks,
+    # the persistent kernel on a 256-CU device) for three of its 16 chunks
+    for c in (0, 7, 15):
+        note(f"partitioned chunk {c}: q_len=1024 kv_len={1024 * (c + 1)} capacity={S}")
+        part = kb.partitioned(qd[:, :, 1024 * c:1024 * (c + 1)].contiguous(), kd, vd, kv_len=1024 * (c + 1))
+        assert_same_bits(bits(part), bits(pre[:, :, 1024 * c:1024 * (c + 1)]), f"partitioned chunk {c}")
+        del part
     rng = np.random.default_rng(seed)
     rows = sample_rows(rng, B, HQ, S, extra=4, fixed=(0, 1, 63, 64, 65, 1023, 1024, 1025, 8191))
     flat = pre.view(-1, D)
